@@ -1,0 +1,322 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert FP8 MoE layer forward on one MI355X.
+
+One step = one forward of the whole layer over one batch (routing, 1x128
+activation quantisation, permutation, fused gate|up GEMM + SwiGLU + FP8
+quantisation, down GEMM, shared expert, combine) on the DeepSeek-V3-shaped
+workload: T=4096 tokens, hidden 7168, 256 routed experts (top-8 sigmoid with
+bias) + 1 shared expert, SwiGLU inter 2048.  Weights are block-quantised to
+FP8 before the timed region (as in training, once per optimizer step); that
+pass, the backward-side block transpose and the dgrad GEMM are timed
+separately and reported under "extra".  Inputs are seeded synthetic tensors
+resident in HBM before timing starts.
+
+Prints ONE JSON line (see the keys below).  Per-kernel times come from HIP
+events recorded on the stream the library launches on, inside the timed
+region.  The CPU baseline times the oracle (test infrastructure) on a
+bounded sample of the same workload and scales it to the full layer.
+
+usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
+METRIC = "MoE-layer fwd tokens/s + FP8 grouped-GEMM TFLOP/s (% MFMA peak), 1 GPU"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", default="dsv3")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extra", action="store_true")
+    return p.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def gemm1_bytes(T, K, H, E, I):
+    """Algorithmic HBM bytes of the fused gate|up launch: activation codes and
+    scales, every expert's gate|up codes and block scales, h codes and scales."""
+    M = T * K
+    return (M * H + M * (H // 128) * 4 + E * 2 * I * H + E * (2 * I // 128) * (H // 128) * 4
+            + M * I + M * (I // 128) * 4)
+
+
+def gemm_flops(M, N, K):
+    return 2.0 * M * N * K
+
+
+def source_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(name, kernel_src):
+    """HBM traffic measured by rocprofv3 counters for this kernel, if the
+    committed measurement was taken on the current kernel source."""
+    f = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+    if not os.path.exists(f):
+        return None
+    rec = json.load(open(f))
+    if rec.get("kernel_source_sha256_16") != source_hash(kernel_src):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def time_op(fn, reps, torch):
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    fn()
+    torch.cuda.synchronize()
+    evs[0].record()
+    for i in range(reps):
+        fn()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    return sum(evs[i].elapsed_time(evs[i + 1]) for i in range(reps)) / reps
+
+
+def extra_rows(cfg, d, fwd, torch, R, synth, reps=5):
+    """Weight quantisation of all experts, and the backward-side block
+    transpose + dY quantisation + dgrad GEMM on the dsv3 expert shapes."""
+    out = {}
+    T, H, E, I = cfg["T"], cfg["H"], cfg["E"], cfg["I"]
+    w13, w2 = d["w13"], d["w2"]
+    q13 = torch.empty(w13.shape, dtype=torch.uint8, device=w13.device)
+    s13 = torch.empty((E, 2 * I // 128, H // 128), dtype=torch.float32, device=w13.device)
+    ms = time_op(lambda: R.quant_weight_128x128_e4m3(w13, q=q13, scale=s13), reps, torch)
+    nbytes = w13.numel() * 3 + s13.numel() * 4
+    out["quant_weight_128x128_w13_all_experts"] = dict(
+        ms=ms, GBps=nbytes / ms / 1e6, frac_hbm=nbytes / ms / 1e6 / HBM_PEAK_GBS, bytes=nbytes)
+    del q13, s13
+    # backward side: gate projection of every expert, stored [2048, 7168]
+    bcfg = dict(synth.get_config("bwd"), I=I // 2)       # [E, 2 * (I/2), H] = [E, 2048, 7168]
+    wg = synth.expert_weights(bcfg, "w13", w13.device, seed=1)
+    wq, ws = R.quant_weight_128x128_e4m3(wg)
+    del wg
+    qt = torch.empty((E, H, I), dtype=torch.uint8, device=wq.device)
+    st = torch.empty((E, H // 128, I // 128), dtype=torch.float32, device=wq.device)
+    ms = time_op(lambda: R.fp8_block_transpose(wq, ws, qt=qt, scale_t=st), reps, torch)
+    nbytes = 2 * (wq.numel() + ws.numel() * 4)
+    out["fp8_block_transpose_e256_2048x7168"] = dict(
+        ms=ms, GBps=nbytes / ms / 1e6, frac_hbm=nbytes / ms / 1e6 / HBM_PEAK_GBS, bytes=nbytes)
+    M = T * cfg["K"]
+    dy = synth.output_grad(M, I, wq.device, seed=0)
+    dyq = torch.empty((M, I), dtype=torch.uint8, device=wq.device)
+    dys = torch.empty((M, I // 128), dtype=torch.float32, device=wq.device)
+    ms_q = time_op(lambda: R.quant_act_1x128_e4m3(dy, q=dyq, scale=dys), reps, torch)
+    nbytes = dy.numel() * 3 + dys.numel() * 4
+    out["quant_act_1x128_dY"] = dict(ms=ms_q, GBps=nbytes / ms_q / 1e6,
+                                     frac_hbm=nbytes / ms_q / 1e6 / HBM_PEAK_GBS, bytes=nbytes)
+    dx = torch.empty((M, H), dtype=torch.float32, device=wq.device)
+    offsets = fwd.buf["offsets"]
+    ms = time_op(lambda: R.grouped_gemm_fp8_blockscaled(dyq, dys, qt, st, offsets, c=dx), reps, torch)
+    fl = gemm_flops(M, H, I)
+    nbytes = M * I + M * (I // 128) * 4 + qt.numel() + st.numel() * 4 + M * H * 4
+    out["dgrad_grouped_gemm_m32768_n7168_k2048"] = dict(
+        ms=ms, TFLOPs=fl / ms / 1e9, frac_mfma=fl / ms / 1e9 / FP8_PEAK_TFLOPS, GBps=nbytes / ms / 1e6,
+        frac_hbm=nbytes / ms / 1e6 / HBM_PEAK_GBS, bytes=nbytes, flops=fl)
+    return out
+
+
+def cpu_baseline(cfg, d, n_experts=2, shared_tokens=128, combine_tokens=256):
+    """The oracle as it stands, on a bounded sample of the workload, scaled to
+    the full layer: routing, activation quantisation and permutation of all
+    tokens; the routed-expert FFN (GEMM1, SwiGLU + quantisation, GEMM2) for
+    `n_experts` experts with all their rows; the shared expert for
+    `shared_tokens` tokens; the combine for `combine_tokens` tokens."""
+    import numpy as np
+    import oracle as O
+    from threadpoolctl import threadpool_info
+    T, H, E, I, K = cfg["T"], cfg["H"], cfg["E"], cfg["I"], cfg["K"]
+    x = d["x"].float().cpu().numpy()
+    logits = d["logits"].cpu().numpy()
+    bias = d["bias"].cpu().numpy() if d["bias"] is not None else None
+    t = {}
+    t0 = time.perf_counter()
+    idx, gate = O.route_sigmoid_bias(logits, bias, K, True)
+    t["route"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    xq, xs = O.quant_act_1x128(x)
+    t["quant_act"] = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    perm = O.permute(idx, E, xq, xs)
+    t["permute"] = time.perf_counter() - t0
+    counts = np.diff(perm["offsets"])
+    order = np.argsort(counts)
+    experts = [int(e) for e in order[len(order) // 2: len(order) // 2 + n_experts]]   # median loads
+    t_exp = 0.0
+    rows_done = 0
+    for e in experts:
+        w13q, w13s = O.quant_weight_128x128(d["w13"][e:e + 1].float().cpu().numpy())   # untimed prep
+        w2q, w2s = O.quant_weight_128x128(d["w2"][e:e + 1].float().cpu().numpy())
+        r0, r1 = perm["offsets"][e], perm["offsets"][e + 1]
+        off = np.array([0, r1 - r0], np.int32)
+        t0 = time.perf_counter()
+        c1, _ = O.grouped_gemm(perm["aq"][r0:r1], perm["as"][r0:r1], w13q, w13s, off, with_mag=False)
+        hq, hs, _ = O.swiglu_quant(c1.astype(np.float32))
+        O.grouped_gemm(hq, hs, w2q, w2s, off, with_mag=False)
+        t_exp += time.perf_counter() - t0
+        rows_done += int(r1 - r0)
+    sw13q, sw13s = O.quant_weight_128x128(d["sw13"].float().cpu().numpy())
+    sw2q, sw2s = O.quant_weight_128x128(d["sw2"].float().cpu().numpy())
+    off = np.array([0, shared_tokens], np.int32)
+    t0 = time.perf_counter()
+    c1, _ = O.grouped_gemm(xq[:shared_tokens], xs[:shared_tokens], sw13q, sw13s, off, with_mag=False)
+    hq, hs, _ = O.swiglu_quant(c1.astype(np.float32))
+    O.grouped_gemm(hq, hs, sw2q, sw2s, off, with_mag=False)
+    t_sh = time.perf_counter() - t0
+    yperm = np.zeros((combine_tokens * K, H))
+    dst = np.arange(combine_tokens * K).reshape(combine_tokens, K)
+    t0 = time.perf_counter()
+    O.combine_ref(yperm, dst, gate[:combine_tokens], np.zeros((combine_tokens, H)))
+    t_comb = time.perf_counter() - t0
+    total = (t["route"] + t["quant_act"] + t["permute"] + t_exp * (T * K) / max(rows_done, 1)
+             + t_sh * T / shared_tokens + t_comb * T / combine_tokens)
+    sampled = sum(t.values()) + t_exp + t_sh + t_comb
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return dict(value=T / total, unit="tokens/s", cores=threads, kind="oracle",
+                sample=(f"oracle layer forward on the {cfg['name']} workload: routing, activation "
+                        f"quantisation and permutation of all {T} tokens; routed-expert FFN for "
+                        f"{n_experts} median-load experts ({rows_done} of {T * K} rows, scaled by rows); "
+                        f"shared expert for {shared_tokens} tokens and combine for {combine_tokens} "
+                        f"tokens (scaled by tokens); {sampled:.1f} s of CPU work measured, "
+                        f"{total:.1f} s estimated for the full layer"),
+                seconds_full_layer_estimate=total)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the expert-parallel multi-GPU path is not part of it)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import routed_experts_fp8_amd as R
+    import synth
+
+    cfg = synth.get_config(args.config)
+    dev = torch.device("cuda:0")
+    T, H, E, I, K = cfg["T"], cfg["H"], cfg["E"], cfg["I"], cfg["K"]
+    log(f"generating {cfg['name']} inputs on the GPU")
+    d = synth.layer_inputs(cfg, dev, seed=0)
+    w = R.quantize_weights(d["w13"], d["w2"], d.get("sw13"), d.get("sw2"))
+    fwd = R.MoEForward(T, H, E, I, cfg["route"], w, dev, fused=True, shared_I=cfg.get("shared_I"))
+    torch.cuda.synchronize()
+    log("warmup")
+    for _ in range(args.warmup):
+        fwd(d["x"], d["logits"], d["bias"])
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    marks = []
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+
+    def on_stage(name):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        marks[-1].append((name, e))
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        s = torch.cuda.Event(enable_timing=True)
+        s.record()
+        marks.append([("start", s)])
+        fwd(d["x"], d["logits"], d["bias"], on_stage=on_stage)
+    end.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    ms_per_step = start.elapsed_time(end) / args.steps
+    stage_ms = {}
+    for step in marks:
+        for (_, a), (name, b) in zip(step[:-1], step[1:]):
+            stage_ms[name] = stage_ms.get(name, 0.0) + a.elapsed_time(b) / args.steps
+
+    tokens_per_s = T / (ms_per_step / 1e3)
+    M = T * K
+    g1_ms = stage_ms["gemm1"]
+    g2_ms = stage_ms["gemm2"]
+    g1_flops = gemm_flops(M, 2 * I, H)
+    g2_flops = gemm_flops(M, H, I)
+    g1_bytes = gemm1_bytes(T, K, H, E, I)
+    g1_gbs = g1_bytes / g1_ms / 1e6
+    gemm = dict(
+        gemm1_swiglu=dict(ms=g1_ms, TFLOPs=g1_flops / g1_ms / 1e9,
+                          frac_mfma=g1_flops / g1_ms / 1e9 / FP8_PEAK_TFLOPS, GBps=g1_gbs,
+                          frac_hbm=g1_gbs / HBM_PEAK_GBS, flops=g1_flops, bytes=g1_bytes),
+        gemm2=dict(ms=g2_ms, TFLOPs=g2_flops / g2_ms / 1e9,
+                   frac_mfma=g2_flops / g2_ms / 1e9 / FP8_PEAK_TFLOPS),
+    )
+    all_gemm_ms = g1_ms + g2_ms
+    all_gemm_flops = g1_flops + g2_flops
+    if cfg.get("shared_I"):
+        Is = cfg["shared_I"]
+        sf1, sf2 = gemm_flops(T, 2 * Is, H), gemm_flops(T, H, Is)
+        gemm["shared_gemm1_swiglu"] = dict(ms=stage_ms["shared_gemm1"],
+                                           TFLOPs=sf1 / stage_ms["shared_gemm1"] / 1e9)
+        gemm["shared_gemm2"] = dict(ms=stage_ms["shared_gemm2"], TFLOPs=sf2 / stage_ms["shared_gemm2"] / 1e9)
+        all_gemm_ms += stage_ms["shared_gemm1"] + stage_ms["shared_gemm2"]
+        all_gemm_flops += sf1 + sf2
+    gemm["all_grouped_gemms"] = dict(ms=all_gemm_ms, TFLOPs=all_gemm_flops / all_gemm_ms / 1e9,
+                                     frac_mfma=all_gemm_flops / all_gemm_ms / 1e9 / FP8_PEAK_TFLOPS)
+
+    traffic = measured_traffic("gemm1_swiglu_dsv3", os.path.join(ROOT, "routed_experts_fp8_amd", "csrc",
+                                                                  "gemm.hip"))
+    roofline = dict(bound="hbm", achieved=g1_gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=g1_gbs / HBM_PEAK_GBS,
+                    traffic=traffic, kernel="grouped_gemm_fp8_swiglu (routed gate|up GEMM + SwiGLU + quant)",
+                    algorithmic_bytes_per_launch=g1_bytes)
+
+    extra = None
+    if not args.no_extra:
+        log("extra rows: weight quantisation, block transpose, dgrad")
+        extra = extra_rows(cfg, d, fwd, torch, R, synth)
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle, bounded sample)")
+        cpu = cpu_baseline(cfg, d)
+
+    line = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "wall_ms_per_step": wall_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3",
+        "data": "synthetic (seeded N(0,1) activations and router logits, N(0,0.006) bf16 weights)",
+        "config": {"workload": cfg["name"], "T": T, "hidden": H, "experts": E, "top_k": K,
+                   "inter": I, "shared_inter": cfg.get("shared_I"), "route": cfg["route"]["mode"]},
+        "gemm_tflops": gemm["all_grouped_gemms"]["TFLOPs"],
+        "gemm_frac_mfma_peak": gemm["all_grouped_gemms"]["frac_mfma"],
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "stages_ms": stage_ms,
+        "gemm": gemm,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

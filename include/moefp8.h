@@ -1,0 +1,267 @@
+/*
+ * moefp8.h -- C ABI of libmoefp8.so, the MI355X (gfx950) routed-expert FP8
+ * MoE FFN layer.
+ *
+ * The operations follow three public write-ups:
+ *   [KANANA-FP8] "Kakao Kanana-2 pre-training deep dive" (devday.kr), the
+ *                paragraph on FP8 Tensor-Core training with fine-grained
+ *                scaling, an all-experts MoE quantisation kernel and a
+ *                transpose kernel for block-quantised weights;
+ *   [DSV3-MOE]   "DeepSeek-V3 technical report summary" (theinnovators.zone),
+ *                section 2.1, DeepSeekMoE bullets (shared + routed experts,
+ *                sigmoid affinity then top-K, per-expert balancing bias, no
+ *                token dropping);
+ *   [DSV3-FP8]   same page, section 2.2, FP8 mixed-precision bullets (FP8
+ *                GEMMs, 1x128 / 128x128 quantisation, promoted accumulation);
+ *   [PANGU-MOGE] "Huawei releases open-weight models trained on Ascend"
+ *                (amuse.peoplentools.com), Mixture-of-Grouped-Experts section
+ *                (equal groups, K' picks per group, one global softmax,
+ *                unselected scores 0, Imbalance Score 0).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Every buffer argument is a DEVICE pointer (memory of the current HIP
+ *    device).  Scalars are passed by value.  Row-major layouts throughout.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is enqueued on it; no entry point synchronises the host.
+ *  - The caller allocates and owns every buffer (including workspaces).  The
+ *    library keeps no pointer after returning; enqueued kernels read and
+ *    write the buffers until the stream reaches them.  No entry point
+ *    allocates device memory.
+ *  - Arguments are checked before anything is enqueued; on any error the
+ *    function returns a non-zero status and launches nothing.  Checks never
+ *    touch the device, so they also run on a host without a GPU.
+ *  - A failed launch returns MOE_ERR_HIP; moe_last_error_detail() gives the
+ *    HIP error text.  Device faults surface at the caller's next
+ *    synchronisation.  With the environment variable MOEFP8_SYNC_CHECK=1
+ *    every entry point synchronises its stream and reports device errors.
+ *  - Preconditions that are NOT checked (undefined results if violated):
+ *    finite inputs; expert ids in [0, E) and distinct within a token;
+ *    group offsets non-decreasing with offsets[0] == 0 and offsets[G] == M.
+ *  - FP8 codes are OCP E4M3FN bytes (bias 7, 3 mantissa bits, max 448, no
+ *    infinities).  Quantisation: amax = max |x| over the tile or block,
+ *    s = fl32(amax / 448) (s = 1 when amax == 0), code =
+ *    RNE_E4M3(clamp(fl32(x / s), -448, 448)) with the sign kept; the value a
+ *    code stands for is decode(code) * s.
+ *  - Pointers to 16-byte vectors (codes, bf16 rows, fp32 rows) must be
+ *    16-byte aligned (MOE_ERR_ALIGN otherwise); index and scale arrays need
+ *    4-byte alignment.
+ */
+#ifndef MOEFP8_H
+#define MOEFP8_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_API __attribute__((visibility("default")))
+
+typedef int32_t moe_status;
+enum {
+  MOE_OK = 0,
+  MOE_ERR_NULL = 1,        /* a required pointer is NULL                    */
+  MOE_ERR_SHAPE = 2,       /* a size is negative, zero where it may not be, */
+                           /* not a multiple of 128, or inconsistent        */
+  MOE_ERR_UNSUPPORTED = 3, /* valid request outside what is implemented    */
+  MOE_ERR_ALIGN = 4,       /* a pointer is not aligned as required          */
+  MOE_ERR_WORKSPACE = 5,   /* the workspace is smaller than required        */
+  MOE_ERR_HIP = 6          /* the HIP runtime reported an error             */
+};
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum {
+  MOE_ROUTE_SIGMOID_BIAS = 0,   /* [DSV3-MOE]   */
+  MOE_ROUTE_SOFTMAX_GROUPED = 1 /* [PANGU-MOGE] */
+} moe_route_mode;
+
+/* Text of a status code (static storage). */
+MOE_API const char* moe_status_string(moe_status s);
+/* Detail of the last error on the calling thread (thread-local storage,
+ * valid until the thread's next call into the library). */
+MOE_API const char* moe_last_error_detail(void);
+
+/*
+ * moe_route -- token -> expert selection.            [DSV3-MOE], [PANGU-MOGE]
+ *
+ *  logits     f32 [T, E]   router scores (the router projection itself is
+ *                          outside this library)
+ *  bias       f32 [E] or NULL (= zeros); SIGMOID_BIAS only
+ *  T >= 0, 1 <= E <= 1024
+ *  SIGMOID_BIAS: 1 <= K <= E; n_groups and k_per_group are ignored.
+ *     s_e = sigmoid(l_e) (binary32 specification: 1 / (1 + E(-x)) with the
+ *     Cody-Waite + degree-7 Taylor exp written out in the library source);
+ *     key_e = fl32(s_e + bias_e); the K largest keys win, equal keys go to
+ *     the lower expert index; slot k holds the k-th largest key.
+ *     gate = s_e (the bias selects but does not weight); if normalize_topk,
+ *     gate_k = fl32(s_k / S) with S summed in slot order in binary32.
+ *  SOFTMAX_GROUPED: E % n_groups == 0, 1 <= k_per_group <= E / n_groups,
+ *     K == n_groups * k_per_group.  Within each group the k_per_group
+ *     largest logits win (equal logits -> lower index); slots are group-major,
+ *     largest first.  gate = softmax over all E experts (computed in float64,
+ *     rounded to float32), not renormalised; normalize_topk must be 0.
+ *  topk_idx   i32 [T, K]   (out)
+ *  topk_gate  f32 [T, K]   (out)
+ * Errors: NULL logits/outputs -> MOE_ERR_NULL; bad sizes -> MOE_ERR_SHAPE;
+ *         E > 1024 -> MOE_ERR_UNSUPPORTED.
+ */
+MOE_API moe_status moe_route(const float* logits, const float* bias, int32_t T, int32_t E, int32_t K,
+                     int32_t n_groups, int32_t k_per_group, moe_route_mode mode,
+                     int32_t normalize_topk, int32_t* topk_idx, float* topk_gate, void* stream);
+
+/*
+ * moe_permute_workspace_size -- bytes of device workspace moe_permute needs
+ * for (T, K, E).  Host-only; never touches the device.
+ */
+MOE_API moe_status moe_permute_workspace_size(int32_t T, int32_t K, int32_t E, size_t* bytes);
+
+/*
+ * moe_permute -- group (token, slot) pairs by expert.       [DSV3-MOE], [PANGU-MOGE]
+ *
+ * No token is dropped and there is no capacity limit or padding: expert e
+ * owns rows [offsets[e], offsets[e+1]) of the permuted operand, in ascending
+ * token order (a stable counting sort of (expert, token) pairs; the result
+ * does not depend on thread scheduling).
+ *
+ *  topk_idx        i32 [T, K]  expert ids (distinct within a token)
+ *  xq, xs          u8 [T, H], f32 [T, H/128]  quantised tokens, or both NULL
+ *                  to compute only the index maps
+ *  expert_offsets  i32 [E+1]   (out) offsets[0] = 0, offsets[E] = T*K
+ *  dst_row         i32 [T, K]  (out) permuted row of pair (t, k)
+ *  src_token       i32 [T*K]   (out) token of permuted row r
+ *  aq, as          u8 [T*K, H], f32 [T*K, H/128] (out; NULL iff xq is NULL)
+ *                  aq[dst_row[t,k]] = xq[t], as[dst_row[t,k]] = xs[t]
+ *  workspace       >= moe_permute_workspace_size(T, K, E) bytes, 16-B aligned
+ *  With T == 0 only expert_offsets (all zeros on return) and the workspace
+ *  are used; the other arrays may be NULL.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (H % 128, K > E, ...),
+ *         MOE_ERR_UNSUPPORTED (E > 1024), MOE_ERR_ALIGN, MOE_ERR_WORKSPACE.
+ */
+MOE_API moe_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t K, int32_t E,
+                       const uint8_t* xq, const float* xs, int32_t H,
+                       int32_t* expert_offsets, int32_t* dst_row, int32_t* src_token,
+                       uint8_t* aq, float* as, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
+/*
+ * quant_act_1x128_e4m3 -- per-(row, 128-column tile) FP8 quantisation of
+ * activations.                                        [KANANA-FP8], [DSV3-FP8]
+ *
+ *  x      f32 or bf16 [rows, cols], cols % 128 == 0 (tiles run along the row,
+ *         the GEMM reduction dimension)
+ *  q      u8  [rows, cols]      (out) E4M3FN codes
+ *  scale  f32 [rows, cols/128]  (out)
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN.
+ */
+MOE_API moe_status quant_act_1x128_e4m3(const void* x, moe_dtype x_dtype, int64_t rows, int32_t cols,
+                                uint8_t* q, float* scale, void* stream);
+
+/*
+ * quant_weight_128x128_e4m3 -- per-128x128-block FP8 quantisation of all G
+ * experts' weights in one launch.                     [KANANA-FP8], [DSV3-FP8]
+ *
+ *  w      f32 or bf16 [G, rows, cols], rows % 128 == cols % 128 == 0; blocks
+ *         anchored at (0, 0)
+ *  q      u8  [G, rows, cols]            (out)
+ *  scale  f32 [G, rows/128, cols/128]    (out)
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN.
+ */
+MOE_API moe_status quant_weight_128x128_e4m3(const void* w, moe_dtype w_dtype, int32_t G, int32_t rows,
+                                     int32_t cols, uint8_t* q, float* scale, void* stream);
+
+/*
+ * grouped_gemm_fp8_blockscaled -- per-group C = A . B_g^T with block-scaled
+ * FP8 operands and promoted accumulation.                        [DSV3-FP8]
+ *
+ *   C[m, n] = sum_kb ( sum_{k in kb} qa[m,k] * qb_g[n,k] ) * sa[m,kb] * sb_g[n/128, kb]
+ * for offsets[g] <= m < offsets[g+1]; kb runs over 128-wide chunks of K.
+ * Each chunk's FP8 dot products come from the matrix cores; the chunk result
+ * is scaled and added to a float32 running sum (one fused multiply-add per
+ * output per chunk), in chunk order.
+ *
+ *  aq  u8 [M, K], as f32 [M, K/128]           activations, 1x128 tiles
+ *  bq  u8 [G, N, K], bs f32 [G, N/128, K/128] weights ([out, in] per group)
+ *  group_offsets i32 [G+1] (device)           offsets[G] == M
+ *  c   f32 or bf16 [M, N] (out); bf16 output is the RNE rounding of the
+ *      float32 result.  Rows of empty groups do not exist; every row of C is
+ *      written.
+ *  Sizes: M >= 0, 1 <= G <= 1024, N % 128 == 0, K % 128 == 0.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED (G > 1024),
+ *         MOE_ERR_ALIGN.
+ */
+MOE_API moe_status grouped_gemm_fp8_blockscaled(const uint8_t* aq, const float* as, const uint8_t* bq,
+                                        const float* bs, const int32_t* group_offsets, int32_t G,
+                                        int64_t M, int32_t N, int32_t K, void* c,
+                                        moe_dtype c_dtype, void* stream);
+
+/*
+ * grouped_gemm_fp8_swiglu -- the gate|up grouped GEMM with SwiGLU and 1x128
+ * FP8 quantisation of the result fused into its epilogue.   [DSV3-FP8]
+ *
+ * Computes, per group, G1 = A . B_g^T exactly as grouped_gemm_fp8_blockscaled
+ * with N = 2I (bit-identical float32 values), then h = silu(g) * u with
+ * g = G1[:, :I], u = G1[:, I:], silu(x) = fl32(x * sigmoid(x)) with the
+ * binary32 sigmoid specification of moe_route, and quantises h in 1x128 tiles
+ * along I.  The float32 G1 is never written.
+ *
+ *  bq  u8 [G, 2I, K]: rows [0, I) are the gate projection, [I, 2I) the up
+ *  hq  u8 [M, I], hs f32 [M, I/128]   (out)
+ *  Sizes: I % 128 == 0, K % 128 == 0.
+ * Errors: as grouped_gemm_fp8_blockscaled.
+ */
+MOE_API moe_status grouped_gemm_fp8_swiglu(const uint8_t* aq, const float* as, const uint8_t* bq,
+                                   const float* bs, const int32_t* group_offsets, int32_t G,
+                                   int64_t M, int32_t I, int32_t K, uint8_t* hq, float* hs,
+                                   void* stream);
+
+/*
+ * swiglu -- standalone SwiGLU + 1x128 FP8 quantisation.           [DSV3-FP8]
+ *
+ *  gate_up  f32 [M, 2I]  (g = columns [0, I), u = columns [I, 2I))
+ *  hq       u8  [M, I]      (out)  codes of h = fl32(silu(g) * u)
+ *  hs       f32 [M, I/128]  (out)
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (I % 128), MOE_ERR_ALIGN.
+ */
+MOE_API moe_status swiglu(const float* gate_up, int64_t M, int32_t I, uint8_t* hq, float* hs,
+                  void* stream);
+
+/*
+ * moe_combine -- gate-weighted sum of each token's expert outputs plus the
+ * shared expert's output, stored as bf16.                        [DSV3-MOE]
+ *
+ *   acc = 0; for k = 0..K-1: acc = fl32(acc + fl32(gate[t,k] * y_perm[dst_row[t,k], n]));
+ *   acc = fl32(acc + shared[t, n]) (if shared != NULL); out[t, n] = bf16_rne(acc)
+ *
+ *  y_perm     f32 [T*K, H]  expert outputs in permuted order
+ *  dst_row    i32 [T, K]    from moe_permute
+ *  topk_gate  f32 [T, K]    from moe_route
+ *  shared     f32 [T, H] or NULL
+ *  out_bf16   u16 [T, H] (out) bf16 bit patterns
+ *  H % 8 == 0.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN.
+ */
+MOE_API moe_status moe_combine(const float* y_perm, const int32_t* dst_row, const float* topk_gate,
+                       const float* shared, int32_t T, int32_t K, int32_t H, uint16_t* out_bf16,
+                       void* stream);
+
+/*
+ * fp8_block_transpose -- transpose of block-quantised weights, codes and
+ * scale grid, as exact bit copies (the backward pass's operand without
+ * re-quantising).                                               [KANANA-FP8]
+ *
+ *  q        u8  [G, rows, cols],      scale   f32 [G, rows/128, cols/128]
+ *  qt       u8  [G, cols, rows] (out), scale_t f32 [G, cols/128, rows/128] (out)
+ *  rows % 128 == cols % 128 == 0.  q and qt must not overlap.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN.
+ */
+MOE_API moe_status fp8_block_transpose(const uint8_t* q, const float* scale, int32_t G, int32_t rows,
+                               int32_t cols, uint8_t* qt, float* scale_t, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEFP8_H */

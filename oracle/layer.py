@@ -33,13 +33,13 @@ def route(logits, bias, rc):
 
 
 def _expert_ffn(aq, as_, offsets, w13q, w13s, w2q, w2s, h_forced=None):
-    c1, _ = grouped_gemm(aq, as_, w13q, w13s, offsets, with_mag=False)
+    c1, mag1 = grouped_gemm(aq, as_, w13q, w13s, offsets, with_mag=True)
     if h_forced is None:
         hq, hs, _ = swiglu_quant(c1.astype(np.float32))
     else:
         hq, hs = h_forced
     c2, mag2 = grouped_gemm(hq, hs, w2q, w2s, offsets, with_mag=True)
-    return dict(c1=c1, hq=hq, hs=hs, c2=c2, mag2=mag2)
+    return dict(c1=c1, mag1=mag1, hq=hq, hs=hs, c2=c2, mag2=mag2)
 
 
 def layer_forward(x, logits, bias, rc, w13q, w13s, w2q, w2s, shared=None,

@@ -1,0 +1,17 @@
+"""MI355X (gfx950) routed-expert FP8 MoE FFN layer.
+
+The computation lives in ``libmoefp8.so`` (hand-written HIP kernels behind a
+C ABI, declared in ``include/moefp8.h``); this package is its thin Python
+binding plus the layer pipeline that sequences the calls.  Importing it
+fails loudly if the library has not been built.
+"""
+
+from ._lib import (MoeError, fp8_block_transpose, grouped_gemm_fp8_blockscaled,
+                   grouped_gemm_fp8_swiglu, moe_combine, moe_permute, moe_permute_workspace_size,
+                   moe_route, quant_act_1x128_e4m3, quant_weight_128x128_e4m3, swiglu, LIB_PATH)
+from .layer import MoEForward, quantize_weights
+
+__all__ = ["MoeError", "fp8_block_transpose", "grouped_gemm_fp8_blockscaled",
+           "grouped_gemm_fp8_swiglu", "moe_combine", "moe_permute", "moe_permute_workspace_size",
+           "moe_route", "quant_act_1x128_e4m3", "quant_weight_128x128_e4m3", "swiglu",
+           "MoEForward", "quantize_weights", "LIB_PATH"]

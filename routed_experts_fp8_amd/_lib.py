@@ -1,0 +1,269 @@
+"""ctypes binding of libmoefp8.so: one Python function per C entry point,
+same names, argument marshalling only (shape/dtype/device checks, output
+allocation when no `out` is given, the current torch stream).  Every step
+of the computation runs in the library's HIP kernels; there is no fallback.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoefp8.so")
+
+MOE_OK = 0
+MOE_F32, MOE_BF16 = 0, 1
+ROUTE_SIGMOID_BIAS, ROUTE_SOFTMAX_GROUPED = 0, 1
+
+_c_void_p = ctypes.c_void_p
+_i32, _i64, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+
+_SIGNATURES = {
+    "moe_status_string": (ctypes.c_char_p, [_i32]),
+    "moe_last_error_detail": (ctypes.c_char_p, []),
+    "moe_route": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                         _c_void_p, _c_void_p, _c_void_p]),
+    "moe_permute_workspace_size": (_i32, [_i32, _i32, _i32, ctypes.POINTER(_sz)]),
+    "moe_permute": (_i32, [_c_void_p, _i32, _i32, _i32, _c_void_p, _c_void_p, _i32, _c_void_p,
+                           _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p]),
+    "quant_act_1x128_e4m3": (_i32, [_c_void_p, _i32, _i64, _i32, _c_void_p, _c_void_p, _c_void_p]),
+    "quant_weight_128x128_e4m3": (_i32, [_c_void_p, _i32, _i32, _i32, _i32, _c_void_p, _c_void_p,
+                                         _c_void_p]),
+    "grouped_gemm_fp8_blockscaled": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
+                                            _i32, _i64, _i32, _i32, _c_void_p, _i32, _c_void_p]),
+    "grouped_gemm_fp8_swiglu": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32,
+                                       _i64, _i32, _i32, _c_void_p, _c_void_p, _c_void_p]),
+    "swiglu": (_i32, [_c_void_p, _i64, _i32, _c_void_p, _c_void_p, _c_void_p]),
+    "moe_combine": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _c_void_p,
+                           _c_void_p]),
+    "fp8_block_transpose": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _i32, _c_void_p, _c_void_p,
+                                   _c_void_p]),
+}
+
+
+class MoeError(RuntimeError):
+    """A non-OK status from libmoefp8."""
+
+    def __init__(self, fn, status, detail):
+        self.status = status
+        super().__init__(f"{fn}: {status_string(status)} ({detail})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m routed_experts_fp8_amd.build` "
+            "(there is no non-HIP fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+
+
+def status_string(s):
+    return lib.moe_status_string(int(s)).decode()
+
+
+def _check(fn, status):
+    if status != MOE_OK:
+        raise MoeError(fn, status, lib.moe_last_error_detail().decode())
+
+
+def _p(t):
+    return None if t is None else _c_void_p(t.data_ptr())
+
+
+def _stream():
+    return _c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _need(t, name, dtype, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+def _out(out, name, shape, dtype, device):
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    return _need(out, name, dtype, shape)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.float32:
+        return MOE_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+# ---------------------------------------------------------------------------
+
+
+def moe_route(logits, bias, K, mode="sigmoid_bias", n_groups=1, k_per_group=None, normalize=True,
+              topk_idx=None, topk_gate=None):
+    """-> (topk_idx int32 [T, K], topk_gate float32 [T, K])."""
+    _need(logits, "logits", torch.float32)
+    T, E = logits.shape
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (E,))
+    m = ROUTE_SIGMOID_BIAS if mode == "sigmoid_bias" else ROUTE_SOFTMAX_GROUPED
+    if m == ROUTE_SOFTMAX_GROUPED:
+        k_per_group = K // n_groups if k_per_group is None else k_per_group
+        normalize = False
+    idx = _out(topk_idx, "topk_idx", (T, K), torch.int32, logits.device)
+    gate = _out(topk_gate, "topk_gate", (T, K), torch.float32, logits.device)
+    _check("moe_route", lib.moe_route(_p(logits), _p(bias), T, E, K, n_groups,
+                                      k_per_group or K, m, int(bool(normalize)), _p(idx), _p(gate),
+                                      _stream()))
+    return idx, gate
+
+
+def moe_permute_workspace_size(T, K, E):
+    n = _sz(0)
+    _check("moe_permute_workspace_size", lib.moe_permute_workspace_size(T, K, E, ctypes.byref(n)))
+    return n.value
+
+
+def moe_permute(topk_idx, E, xq=None, xs=None, out=None, workspace=None):
+    """-> dict(offsets [E+1], dst_row [T, K], src_token [T*K], aq, as)."""
+    _need(topk_idx, "topk_idx", torch.int32)
+    T, K = topk_idx.shape
+    dev = topk_idx.device
+    out = dict(out or {})
+    H = 0
+    if xq is not None:
+        _need(xq, "xq", torch.uint8)
+        H = xq.shape[1]
+        _need(xs, "xs", torch.float32, (T, H // 128))
+        if xq.shape[0] != T:
+            raise ValueError("xq rows must equal T")
+    res = {
+        "offsets": _out(out.get("offsets"), "offsets", (E + 1,), torch.int32, dev),
+        "dst_row": _out(out.get("dst_row"), "dst_row", (T, K), torch.int32, dev),
+        "src_token": _out(out.get("src_token"), "src_token", (T * K,), torch.int32, dev),
+    }
+    if xq is not None:
+        res["aq"] = _out(out.get("aq"), "aq", (T * K, H), torch.uint8, dev)
+        res["as"] = _out(out.get("as"), "as", (T * K, H // 128), torch.float32, dev)
+    need = moe_permute_workspace_size(T, K, E)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8)
+    _check("moe_permute", lib.moe_permute(
+        _p(topk_idx), T, K, E, _p(xq), _p(xs), H, _p(res["offsets"]), _p(res["dst_row"]),
+        _p(res["src_token"]), _p(res.get("aq")), _p(res.get("as")), _p(workspace),
+        workspace.numel(), _stream()))
+    return res
+
+
+def quant_act_1x128_e4m3(x, q=None, scale=None):
+    """x float32/bf16 [rows, cols] -> (codes uint8 [rows, cols], scales f32 [rows, cols/128])."""
+    code = _dtype_code(x)
+    _need(x, "x", x.dtype)
+    rows, cols = x.shape
+    q = _out(q, "q", (rows, cols), torch.uint8, x.device)
+    scale = _out(scale, "scale", (rows, cols // 128), torch.float32, x.device)
+    _check("quant_act_1x128_e4m3", lib.quant_act_1x128_e4m3(_p(x), code, rows, cols, _p(q),
+                                                            _p(scale), _stream()))
+    return q, scale
+
+
+def quant_weight_128x128_e4m3(w, q=None, scale=None):
+    """w float32/bf16 [G, rows, cols] -> (codes [G, rows, cols], scales [G, rows/128, cols/128])."""
+    code = _dtype_code(w)
+    _need(w, "w", w.dtype)
+    G, rows, cols = w.shape
+    q = _out(q, "q", (G, rows, cols), torch.uint8, w.device)
+    scale = _out(scale, "scale", (G, rows // 128, cols // 128), torch.float32, w.device)
+    _check("quant_weight_128x128_e4m3", lib.quant_weight_128x128_e4m3(
+        _p(w), code, G, rows, cols, _p(q), _p(scale), _stream()))
+    return q, scale
+
+
+def _gemm_operands(aq, as_, bq, bs, offsets):
+    _need(aq, "aq", torch.uint8)
+    M, K = aq.shape
+    _need(as_, "as", torch.float32, (M, K // 128))
+    _need(bq, "bq", torch.uint8)
+    G, N, K2 = bq.shape
+    if K2 != K:
+        raise ValueError(f"bq reduction dim {K2} != aq's {K}")
+    _need(bs, "bs", torch.float32, (G, N // 128, K // 128))
+    _need(offsets, "group_offsets", torch.int32, (G + 1,))
+    return M, K, G, N
+
+
+def grouped_gemm_fp8_blockscaled(aq, as_, bq, bs, offsets, out_dtype=torch.float32, c=None):
+    """C[M, N] = per-group A . B_g^T with block scales (float32 or bf16 output)."""
+    M, K, G, N = _gemm_operands(aq, as_, bq, bs, offsets)
+    c = _out(c, "c", (M, N), out_dtype, aq.device)
+    _check("grouped_gemm_fp8_blockscaled", lib.grouped_gemm_fp8_blockscaled(
+        _p(aq), _p(as_), _p(bq), _p(bs), _p(offsets), G, M, N, K, _p(c), _dtype_code(c),
+        _stream()))
+    return c
+
+
+def grouped_gemm_fp8_swiglu(aq, as_, bq, bs, offsets, hq=None, hs=None):
+    """Gate|up GEMM with fused SwiGLU + 1x128 quantisation -> (hq [M, I], hs [M, I/128])."""
+    M, K, G, N = _gemm_operands(aq, as_, bq, bs, offsets)
+    I = N // 2
+    hq = _out(hq, "hq", (M, I), torch.uint8, aq.device)
+    hs = _out(hs, "hs", (M, I // 128), torch.float32, aq.device)
+    _check("grouped_gemm_fp8_swiglu", lib.grouped_gemm_fp8_swiglu(
+        _p(aq), _p(as_), _p(bq), _p(bs), _p(offsets), G, M, I, K, _p(hq), _p(hs), _stream()))
+    return hq, hs
+
+
+def swiglu(gate_up, hq=None, hs=None):
+    """gate_up float32 [M, 2I] -> (hq uint8 [M, I], hs float32 [M, I/128])."""
+    _need(gate_up, "gate_up", torch.float32)
+    M, twoI = gate_up.shape
+    I = twoI // 2
+    hq = _out(hq, "hq", (M, I), torch.uint8, gate_up.device)
+    hs = _out(hs, "hs", (M, I // 128), torch.float32, gate_up.device)
+    _check("swiglu", lib.swiglu(_p(gate_up), M, I, _p(hq), _p(hs), _stream()))
+    return hq, hs
+
+
+def moe_combine(y_perm, dst_row, topk_gate, shared=None, out=None):
+    """-> y bf16 [T, H] = sum_k gate * y_perm[dst_row] (+ shared)."""
+    _need(y_perm, "y_perm", torch.float32)
+    _need(dst_row, "dst_row", torch.int32)
+    T, K = dst_row.shape
+    H = y_perm.shape[1]
+    _need(topk_gate, "topk_gate", torch.float32, (T, K))
+    if y_perm.shape[0] != T * K:
+        raise ValueError("y_perm must have T*K rows")
+    if shared is not None:
+        _need(shared, "shared", torch.float32, (T, H))
+    out = _out(out, "out", (T, H), torch.bfloat16, y_perm.device)
+    _check("moe_combine", lib.moe_combine(_p(y_perm), _p(dst_row), _p(topk_gate), _p(shared), T, K,
+                                          H, _p(out), _stream()))
+    return out
+
+
+def fp8_block_transpose(q, scale, qt=None, scale_t=None):
+    """(q [G, R, C], s [G, R/128, C/128]) -> (q^T [G, C, R], s^T [G, C/128, R/128])."""
+    _need(q, "q", torch.uint8)
+    G, R, C = q.shape
+    _need(scale, "scale", torch.float32, (G, R // 128, C // 128))
+    qt = _out(qt, "qt", (G, C, R), torch.uint8, q.device)
+    scale_t = _out(scale_t, "scale_t", (G, C // 128, R // 128), torch.float32, q.device)
+    _check("fp8_block_transpose", lib.fp8_block_transpose(_p(q), _p(scale), G, R, C, _p(qt),
+                                                          _p(scale_t), _stream()))
+    return qt, scale_t

@@ -1,0 +1,196 @@
+// FP8 quantisers: 1x128 activation tiles and 128x128 weight blocks of every
+// expert in one launch ([KANANA-FP8] all-experts MoE quantisation kernel;
+// [DSV3-FP8] tile/block granularity).  Both are single coalesced HBM passes:
+// each value is read once and its code written once.
+#include "device_common.h"
+#include "host_common.h"
+
+namespace moefp8 {
+namespace {
+
+// Input element access: 16-byte vectors of 8 bf16 or 4 fp32 values.
+template <typename T> struct Vec;
+template <> struct Vec<uint16_t> {
+  static constexpr int kElems = 8;
+  __device__ static void unpack(const uint4& v, float* out) {
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      out[2 * i] = __uint_as_float(w[i] << 16);
+      out[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+template <> struct Vec<float> {
+  static constexpr int kElems = 4;
+  __device__ static void unpack(const uint4& v, float* out) {
+    out[0] = __uint_as_float(v.x);
+    out[1] = __uint_as_float(v.y);
+    out[2] = __uint_as_float(v.z);
+    out[3] = __uint_as_float(v.w);
+  }
+};
+
+template <int N>
+__device__ __forceinline__ void store_codes(uint8_t* dst, const uint32_t* c);
+template <>
+__device__ __forceinline__ void store_codes<8>(uint8_t* dst, const uint32_t* c) {
+  uint2 v;
+  v.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+  v.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+  *reinterpret_cast<uint2*>(dst) = v;
+}
+template <>
+__device__ __forceinline__ void store_codes<4>(uint8_t* dst, const uint32_t* c) {
+  *reinterpret_cast<uint32_t*>(dst) = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+}
+
+// ---------------------------------------------------------------------------
+// 1x128 tiles.  One lane owns one 16-byte input vector; the 128/kElems lanes
+// of a tile (16 for bf16, 32 for fp32, always an aligned lane group) reduce
+// their amax with cross-lane shuffles.  Grid-stride over vectors, unrolled so
+// that each lane keeps several 16-byte loads in flight.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void quant_act_kernel(const T* __restrict__ x, int64_t n_vec,
+                                                        uint8_t* __restrict__ q,
+                                                        float* __restrict__ scale) {
+  constexpr int E = Vec<T>::kElems;
+  constexpr int LPT = 128 / E;  // lanes per tile
+  constexpr int U = 4;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  const int64_t base = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const uint4* xv = reinterpret_cast<const uint4*>(x);
+  for (int64_t v0 = base; v0 - threadIdx.x % 64 < n_vec; v0 += stride * U) {
+    uint4 raw[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + u * stride;
+      raw[u] = v < n_vec ? load16_nt(xv + v) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t v = v0 + u * stride;
+      float f[E];
+      Vec<T>::unpack(raw[u], f);
+      float amax = 0.0f;
+#pragma unroll
+      for (int i = 0; i < E; ++i) amax = fmaxf(amax, fabsf(f[i]));
+      amax = group_max<LPT>(amax);  // whole wave participates (uniform control)
+      if (v < n_vec) {
+        const float s = scale_from_amax(amax);
+        uint32_t c[E];
+#pragma unroll
+        for (int i = 0; i < E; ++i) c[i] = quantize(f[i], s);
+        store_codes<E>(q + v * E, c);
+        if ((threadIdx.x % LPT) == 0) scale[v / LPT] = s;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 128x128 blocks, one 256-thread workgroup per block (all experts in one
+// grid).  Each thread holds its share of the block in registers (32 KB of
+// bf16 or 64 KB of fp32 per block), the block amax is reduced in-wave and
+// across the 4 waves through LDS, then codes are written from registers.
+// Loads are 16-byte vectors; a wave covers whole 256/512-byte row segments.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void quant_weight_kernel(const T* __restrict__ w, int rows,
+                                                           int cols, uint8_t* __restrict__ q,
+                                                           float* __restrict__ scale) {
+  constexpr int E = Vec<T>::kElems;
+  constexpr int VPR = 128 / E;              // vectors per block row
+  constexpr int NV = 128 * VPR / 256;       // vectors per thread
+  const int bc = cols / 128, br = rows / 128;
+  const int64_t blk = blockIdx.x;
+  const int bj = (int)(blk % bc);
+  const int bi = (int)((blk / bc) % br);
+  const int64_t g = blk / ((int64_t)bc * br);
+  const int64_t gbase = g * rows * (int64_t)cols;
+  const int tid = threadIdx.x;
+  uint4 raw[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int id = i * 256 + tid;
+    const int r = id / VPR, cv = id % VPR;
+    const int64_t off = gbase + (int64_t)(bi * 128 + r) * cols + bj * 128 + cv * E;
+    raw[i] = load16_nt(w + off);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    float f[E];
+    Vec<T>::unpack(raw[i], f);
+#pragma unroll
+    for (int k = 0; k < E; ++k) amax = fmaxf(amax, fabsf(f[k]));
+  }
+  amax = group_max<64>(amax);
+  __shared__ float red[4];
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float s = scale_from_amax(amax);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int id = i * 256 + tid;
+    const int r = id / VPR, cv = id % VPR;
+    const int64_t off = gbase + (int64_t)(bi * 128 + r) * cols + bj * 128 + cv * E;
+    float f[E];
+    Vec<T>::unpack(raw[i], f);
+    uint32_t c[E];
+#pragma unroll
+    for (int k = 0; k < E; ++k) c[k] = quantize(f[k], s);
+    store_codes<E>(q + off, c);
+  }
+  if (tid == 0) scale[blk] = s;  // [G, rows/128, cols/128] row-major == blk order
+}
+
+}  // namespace
+}  // namespace moefp8
+
+using namespace moefp8;
+
+extern "C" moe_status quant_act_1x128_e4m3(const void* x, moe_dtype x_dtype, int64_t rows,
+                                           int32_t cols, uint8_t* q, float* scale, void* stream) {
+  clear_detail();
+  MOE_REQUIRE(x_dtype == MOE_F32 || x_dtype == MOE_BF16, MOE_ERR_UNSUPPORTED, "x_dtype %d", (int)x_dtype);
+  MOE_REQUIRE(rows >= 0 && cols > 0 && cols % 128 == 0, MOE_ERR_SHAPE,
+              "rows=%lld cols=%d (cols must be a positive multiple of 128)", (long long)rows, cols);
+  if (rows == 0) return MOE_OK;
+  MOE_REQUIRE(x && q && scale, MOE_ERR_NULL, "x, q and scale are required");
+  MOE_REQUIRE(aligned(x, 16) && aligned(q, 16) && aligned(scale, 4), MOE_ERR_ALIGN,
+              "x and q need 16-byte alignment, scale 4-byte");
+  hipStream_t st = as_stream(stream);
+  const int elems = x_dtype == MOE_BF16 ? 8 : 4;
+  const int64_t n_vec = rows * (int64_t)cols / elems;
+  const int64_t blocks_needed = (n_vec + 255) / 256;
+  const unsigned grid = (unsigned)(blocks_needed < 8192 ? blocks_needed : 8192);
+  if (x_dtype == MOE_BF16)
+    quant_act_kernel<uint16_t><<<grid, 256, 0, st>>>((const uint16_t*)x, n_vec, q, scale);
+  else
+    quant_act_kernel<float><<<grid, 256, 0, st>>>((const float*)x, n_vec, q, scale);
+  return after_launch("quant_act_1x128_e4m3", st);
+}
+
+extern "C" moe_status quant_weight_128x128_e4m3(const void* w, moe_dtype w_dtype, int32_t G,
+                                                int32_t rows, int32_t cols, uint8_t* q,
+                                                float* scale, void* stream) {
+  clear_detail();
+  MOE_REQUIRE(w_dtype == MOE_F32 || w_dtype == MOE_BF16, MOE_ERR_UNSUPPORTED, "w_dtype %d", (int)w_dtype);
+  MOE_REQUIRE(G >= 0 && rows > 0 && cols > 0 && rows % 128 == 0 && cols % 128 == 0, MOE_ERR_SHAPE,
+              "G=%d rows=%d cols=%d (rows, cols positive multiples of 128)", G, rows, cols);
+  if (G == 0) return MOE_OK;
+  MOE_REQUIRE(w && q && scale, MOE_ERR_NULL, "w, q and scale are required");
+  MOE_REQUIRE(aligned(w, 16) && aligned(q, 16) && aligned(scale, 4), MOE_ERR_ALIGN,
+              "w and q need 16-byte alignment, scale 4-byte");
+  const int64_t nblk = (int64_t)G * (rows / 128) * (cols / 128);
+  MOE_REQUIRE(nblk < (1LL << 31), MOE_ERR_UNSUPPORTED, "too many blocks (%lld)", (long long)nblk);
+  hipStream_t st = as_stream(stream);
+  if (w_dtype == MOE_BF16)
+    quant_weight_kernel<uint16_t><<<(unsigned)nblk, 256, 0, st>>>((const uint16_t*)w, rows, cols, q, scale);
+  else
+    quant_weight_kernel<float><<<(unsigned)nblk, 256, 0, st>>>((const float*)w, rows, cols, q, scale);
+  return after_launch("quant_weight_128x128_e4m3", st);
+}

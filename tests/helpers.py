@@ -1,0 +1,99 @@
+"""Shared helpers of the parity tests: device/host transfers, the tolerance
+rules, and the seeded random inputs used by the per-kernel tests."""
+
+import numpy as np
+import torch
+
+from oracle import e4m3_decode
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def np_(t):
+    """Host numpy copy of a tensor (bf16 becomes its exact float32 value)."""
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        t = t.float()
+    return t.cpu().numpy()
+
+
+def bf16_bits(t):
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def to_dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a)).to(dev())
+    return t if dtype is None else t.to(dtype)
+
+
+def assert_gemm_close(c_gpu, C, Mag, rtol=1e-4, what="gemm"):
+    """Componentwise rule for float32 GEMM outputs: |c - C| <= rtol * (|A||B|)
+    where (|A||B|) is the oracle's magnitude sum of the same dequantised
+    operands (the relative error of a sum is unbounded under cancellation;
+    relative to the magnitude sum it is what floating point guarantees)."""
+    c = np.asarray(c_gpu, np.float64)
+    err = np.abs(c - C)
+    bound = rtol * Mag + 1e-30
+    bad = err > bound
+    assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} outside {rtol} x magnitude; "
+                           f"worst ratio {np.max(err / bound):.3g}")
+    return float(np.max(err / (Mag + 1e-30)))
+
+
+def bf16_ulp_distance(a_bits, b_bits):
+    """Distance in bf16 units in the last place between two bit patterns
+    (ordered integer mapping of the sign-magnitude encoding)."""
+    def ordered(b):
+        b = b.astype(np.int32)
+        return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+    return np.abs(ordered(a_bits) - ordered(b_bits))
+
+
+def e4m3_code_distance(a, b):
+    """Distance between E4M3 codes along the number line (adjacent codes -> 1;
+    +0 and -0 are the same point)."""
+    def ordered(c):
+        c = c.astype(np.int32)
+        return np.where(c & 0x80, -(c & 0x7F), c & 0x7F)
+    return np.abs(ordered(a) - ordered(b))
+
+
+def dequant_rows(q, s):
+    rows, cols = q.shape
+    return (e4m3_decode(q).reshape(rows, -1, 128) * s[:, :, None].astype(np.float64)).reshape(rows, cols)
+
+
+def rand_offsets(rng, sizes):
+    return np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+
+
+def check_hidden(hq, hs, C1, Mag1, hq_o, tol=1e-4):
+    """Validity of GPU FP8 codes/scales of h = silu(g) * u computed from a
+    float32 GEMM result, against the oracle's float64 gate|up output C1 and
+    its magnitude sums Mag1.
+
+    The GEMM bar allows |g_gpu - g| <= tol * Mag_g (same for u), hence
+    |h_gpu - h| <= dh = tol * (|silu(g)| Mag_u + 1.1 |u| Mag_g) (|silu'| <= 1.1)
+    plus a few float32 roundings.  The GPU's dequantised h must then lie within
+    the quantisation bound of h_gpu (half a code step: 2^-4 |h| for normal
+    codes, 2^-10 s for subnormal ones), and each tile scale within dh_max/448
+    of the oracle's.  Returns (fraction of codes that differ from the oracle's,
+    mask of rows with any differing code)."""
+    I = C1.shape[1] // 2
+    g, u = C1[:, :I], C1[:, I:]
+    silu = g / (1.0 + np.exp(-g))
+    h = silu * u
+    dh = tol * (np.abs(silu) * Mag1[:, I:] + 1.1 * np.abs(u) * Mag1[:, :I]) + 2.0 ** -20 * np.abs(h)
+    srep = np.repeat(np.asarray(hs, np.float64), 128, axis=1)
+    deq = dequant_rows(hq, hs)
+    bound = 2.0 ** -4 * (np.abs(h) + dh) + 2.0 ** -10 * srep + dh + 1e-300
+    assert np.all(np.abs(deq - h) <= bound), f"h outside bound: worst ratio {np.max(np.abs(deq - h) / bound):.3g}"
+    rows = h.shape[0]
+    amax = np.abs(h).reshape(rows, -1, 128).max(axis=2)
+    dmax = dh.reshape(rows, -1, 128).max(axis=2)
+    s_o = np.where(amax == 0, 1.0, amax / 448.0)
+    assert np.all(np.abs(hs - s_o) <= (dmax / 448.0) * 1.001 + 2.0 ** -22 * s_o), "h scales outside bound"
+    diff = hq != hq_o
+    return float(diff.mean()), diff.any(axis=1)

@@ -1,0 +1,130 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/moefp8.h declares, reports workspace sizes, and
+rejects bad arguments with the documented status before touching the device.
+Every call here fails validation or is an empty problem, so no kernel is
+ever launched."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from routed_experts_fp8_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = open(os.path.join(ROOT, "include", "moefp8.h")).read()
+DECLARED = re.findall(r"^MOE_API\s+[\w\s\*]*?\b(\w+)\s*\(", HEADER, flags=re.M)
+
+OK, NULL, SHAPE, UNSUP, ALIGN, WS = 0, 1, 2, 3, 4, 5
+P = ctypes.c_void_p(0x10000)          # aligned non-NULL fake device pointer (never dereferenced)
+PM = ctypes.c_void_p(0x10004)         # 4-byte aligned, not 16-byte aligned
+N0 = None
+S = None                              # null stream
+
+
+def test_every_declared_symbol_is_exported():
+    assert len(DECLARED) == 12, DECLARED
+    for name in DECLARED:
+        assert hasattr(L.lib, name), name
+    assert set(DECLARED) == set(L._SIGNATURES)
+
+
+def test_status_strings():
+    for s in range(7):
+        assert L.status_string(s).startswith("MOE_")
+    assert "unknown" in L.status_string(99)
+
+
+def test_workspace_size():
+    n = ctypes.c_size_t(0)
+    assert L.lib.moe_permute_workspace_size(4096, 8, 256, ctypes.byref(n)) == OK
+    assert n.value == 2 * 16 * 256 * 4 + 256
+    assert L.lib.moe_permute_workspace_size(0, 1, 1, ctypes.byref(n)) == OK
+    assert L.lib.moe_permute_workspace_size(10, 9, 8, ctypes.byref(n)) == SHAPE
+    assert L.lib.moe_permute_workspace_size(10, 8, 2048, ctypes.byref(n)) == UNSUP
+    assert L.lib.moe_permute_workspace_size(10, 8, 64, None) == NULL
+
+
+def _detail():
+    return L.lib.moe_last_error_detail().decode()
+
+
+def test_quant_errors():
+    f = L.lib.quant_act_1x128_e4m3
+    assert f(P, 0, 4, 100, P, P, S) == SHAPE and "cols" in _detail()
+    assert f(P, 0, -1, 128, P, P, S) == SHAPE
+    assert f(P, 7, 4, 128, P, P, S) == UNSUP
+    assert f(N0, 0, 4, 128, P, P, S) == NULL
+    assert f(PM, 1, 4, 128, P, P, S) == ALIGN
+    assert f(N0, 0, 0, 128, N0, N0, S) == OK          # empty: nothing to do
+    g = L.lib.quant_weight_128x128_e4m3
+    assert g(P, 0, 2, 100, 128, P, P, S) == SHAPE
+    assert g(P, 0, 2, 128, 130, P, P, S) == SHAPE
+    assert g(P, 0, 2, 128, 128, N0, P, S) == NULL
+    assert g(P, 0, 2, 128, 128, PM, P, S) == ALIGN
+    assert g(N0, 0, 0, 128, 128, N0, N0, S) == OK
+
+
+def test_route_errors():
+    f = L.lib.moe_route
+    sig, grp = L.ROUTE_SIGMOID_BIAS, L.ROUTE_SOFTMAX_GROUPED
+    assert f(P, N0, 4, 2048, 8, 1, 8, sig, 1, P, P, S) == UNSUP
+    assert f(P, N0, 4, 16, 17, 1, 17, sig, 1, P, P, S) == SHAPE
+    assert f(P, N0, 4, 16, 0, 1, 0, sig, 1, P, P, S) == SHAPE
+    assert f(P, N0, 4, 18, 4, 4, 1, grp, 0, P, P, S) == SHAPE      # E % G
+    assert f(P, N0, 4, 16, 8, 4, 1, grp, 0, P, P, S) == SHAPE      # K != G*K'
+    assert f(P, N0, 4, 16, 20, 4, 5, grp, 0, P, P, S) == SHAPE      # K' > E/G
+    assert f(P, N0, 4, 16, 4, 4, 1, grp, 1, P, P, S) == UNSUP      # no renormalisation
+    assert f(N0, N0, 4, 16, 4, 1, 4, sig, 1, P, P, S) == NULL
+    assert f(P, N0, 0, 16, 4, 1, 4, sig, 1, N0, N0, S) == OK        # T = 0
+    assert f(P, N0, 4, 16, 4, 1, 4, 9, 1, P, P, S) == UNSUP
+
+
+def test_permute_errors():
+    f = L.lib.moe_permute
+    assert f(P, 8, 9, 8, N0, N0, 0, P, P, P, N0, N0, P, 1 << 20, S) == SHAPE       # K > E
+    assert f(P, 8, 2, 4096, N0, N0, 0, P, P, P, N0, N0, P, 1 << 20, S) == UNSUP    # E > 1024
+    assert f(P, 8, 2, 8, P, N0, 128, P, P, P, P, P, P, 1 << 20, S) == NULL         # partial gather set
+    assert f(P, 8, 2, 8, P, P, 100, P, P, P, P, P, P, 1 << 20, S) == SHAPE         # H % 128
+    assert f(P, 8, 2, 8, PM, P, 128, P, P, P, P, P, P, 1 << 20, S) == ALIGN
+    assert f(P, 8, 2, 8, N0, N0, 0, P, P, P, N0, N0, P, 16, S) == WS
+    assert f(P, 8, 2, 8, N0, N0, 0, N0, P, P, N0, N0, P, 1 << 20, S) == NULL
+
+
+def test_gemm_errors():
+    f = L.lib.grouped_gemm_fp8_blockscaled
+    assert f(P, P, P, P, P, 4, 64, 100, 128, P, 0, S) == SHAPE
+    assert f(P, P, P, P, P, 4, 64, 128, 130, P, 0, S) == SHAPE
+    assert f(P, P, P, P, P, 2048, 64, 128, 128, P, 0, S) == UNSUP
+    assert f(P, P, P, P, P, 0, 64, 128, 128, P, 0, S) == SHAPE
+    assert f(P, P, P, P, N0, 4, 64, 128, 128, P, 0, S) == NULL
+    assert f(P, P, P, P, P, 4, 64, 128, 128, N0, 0, S) == NULL
+    assert f(PM, P, P, P, P, 4, 64, 128, 128, P, 0, S) == ALIGN
+    assert f(P, P, P, P, P, 4, 64, 128, 128, P, 5, S) == UNSUP
+    assert f(N0, N0, N0, N0, P, 4, 0, 128, 128, N0, 0, S) == OK                    # M = 0
+    g = L.lib.grouped_gemm_fp8_swiglu
+    assert g(P, P, P, P, P, 4, 64, 100, 128, P, P, S) == SHAPE
+    assert g(P, P, P, P, P, 4, 64, 128, 128, P, N0, S) == NULL
+
+
+def test_swiglu_combine_transpose_errors():
+    assert L.lib.swiglu(P, 4, 100, P, P, S) == SHAPE
+    assert L.lib.swiglu(N0, 4, 128, P, P, S) == NULL
+    assert L.lib.swiglu(N0, 0, 128, N0, N0, S) == OK
+    c = L.lib.moe_combine
+    assert c(P, P, P, N0, 4, 2, 12, P, S) == SHAPE
+    assert c(P, P, P, PM, 4, 2, 16, P, S) == ALIGN
+    assert c(N0, P, P, N0, 4, 2, 16, P, S) == NULL
+    assert c(N0, N0, N0, N0, 0, 2, 16, N0, S) == OK
+    t = L.lib.fp8_block_transpose
+    assert t(P, P, 2, 100, 128, P, P, S) == SHAPE
+    assert t(P, P, 2, 128, 128, N0, P, S) == NULL
+    assert t(P, P, 2, 128, 128, PM, P, S) == ALIGN
+    assert t(N0, N0, 0, 128, 128, N0, N0, S) == OK
+
+
+def test_binding_requires_device_tensors():
+    import torch
+    with pytest.raises((ValueError, TypeError)):
+        L.quant_act_1x128_e4m3(torch.zeros(4, 128))

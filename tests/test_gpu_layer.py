@@ -1,0 +1,141 @@
+"""End-to-end parity of the layer forward (the launch sequence the bench
+times) against the oracle's independent evaluation of the same layer.
+
+Rule for the bf16 output y:
+  * every intermediate that is integer or FP8 (routing, activation codes,
+    permutation) must match the oracle bit for bit;
+  * the hidden state h is quantised from a float32 GEMM result, so its FP8
+    codes may differ from the oracle's only by one step next to a rounding
+    boundary (rare) and its scales only by float32 rounding;
+  * tokens whose every h code matches the oracle: y within 1 bf16 ulp of the
+    oracle's y (rounded once from float64);
+  * tokens with a boundary flip in h: |y - y_oracle| within 1 bf16 ulp plus
+    the effect of the flipped codes through the down projection
+    (sum_k gate * |W2| . |dequant difference|) plus the GEMM tolerance.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import routed_experts_fp8_amd as R
+import synth
+from helpers import bf16_bits, bf16_ulp_distance, check_hidden, dev, dequant_rows, np_
+
+pytestmark = pytest.mark.gpu
+
+
+def _variant(name):
+    cfg = synth.get_config("tiny")
+    if name == "tiny_sigmoid_shared":
+        cfg.update(T=200, E=16, K=4, I=256, route=dict(mode="sigmoid_bias", K=4, normalize=True),
+                   bias_std=0.01, shared_I=256, x_dtype="bf16", w_dtype="bf16")
+    if name == "small_moge":
+        cfg.update(T=512, H=1024, E=32, I=384, K=8, route=dict(mode="softmax_grouped", n_groups=8,
+                                                                 k_per_group=1),
+                   x_dtype="bf16", w_dtype="bf16")
+    return cfg
+
+
+def run_layer(cfg, fused, seed=0):
+    d = synth.layer_inputs(cfg, dev(), seed=seed)
+    w = R.quantize_weights(d["w13"], d["w2"], d.get("sw13"), d.get("sw2"))
+    fwd = R.MoEForward(cfg["T"], cfg["H"], cfg["E"], cfg["I"], cfg["route"], w, dev(), fused=fused,
+                       shared_I=cfg.get("shared_I"))
+    y = fwd(d["x"], d["logits"], d["bias"])
+    torch.cuda.synchronize()
+    return d, w, fwd, y
+
+
+def check_layer_against_oracle(cfg, d, w, fwd, y):
+    x = np_(d["x"])
+    logits = np_(d["logits"])
+    bias = None if d["bias"] is None else np_(d["bias"])
+    wq = {k: np_(v) for k, v in w.items()}
+    # weights: the GPU's quantised weights must equal the oracle's (checked),
+    # then the oracle layer runs on its own quantised weights
+    w13q, w13s = O.quant_weight_128x128(np_(d["w13"]))
+    w2q, w2s = O.quant_weight_128x128(np_(d["w2"]))
+    assert np.array_equal(wq["w13q"], w13q) and np.array_equal(wq["w13s"], w13s)
+    assert np.array_equal(wq["w2q"], w2q) and np.array_equal(wq["w2s"], w2s)
+    shared = None
+    if cfg.get("shared_I"):
+        a, b = O.quant_weight_128x128(np_(d["sw13"]))
+        c, e = O.quant_weight_128x128(np_(d["sw2"]))
+        shared = (a, b, c, e)
+    ref = O.layer_forward(x, logits, bias, cfg["route"], w13q, w13s, w2q, w2s, shared=shared)
+    b = {k: np_(v) for k, v in fwd.buf.items()}
+    assert np.array_equal(b["idx"], ref["topk_idx"])
+    if cfg["route"]["mode"] == "sigmoid_bias":
+        assert np.array_equal(b["gate"], ref["topk_gate"])
+    else:
+        assert np.all(np.abs(b["gate"] - ref["topk_gate"]) <= np.spacing(np.abs(ref["topk_gate"])))
+    for k_gpu, k_ref in (("xq", "xq"), ("xs", "xs"), ("offsets", "offsets"), ("dst_row", "dst_row"),
+                         ("src_token", "src_token"), ("aq", "aq"), ("as_", "as")):
+        assert np.array_equal(b[k_gpu], ref[k_ref]), k_gpu
+
+    T, K = ref["dst_row"].shape
+    H = x.shape[1]
+    # hidden state: codes valid under the GEMM tolerance (boundary flips only)
+    frac, row_dirty = check_hidden(b["hq"], b["hs"], ref["c1"], ref["mag1"], ref["hq"])
+    assert frac < 0.01, frac
+    dh = np.abs(dequant_rows(b["hq"], b["hs"]) - dequant_rows(ref["hq"], ref["hs"]))
+    dh[~row_dirty] = 0.0
+    shared_dirty = np.zeros(T, bool)
+    dsh = None
+    if shared is not None:
+        sfrac, shared_dirty = check_hidden(b["shq"], b["shs"], ref["shared_c1"], ref["shared_mag1"],
+                                           ref["shared_hq"])
+        assert sfrac < 0.01, sfrac
+        dsh = np.abs(dequant_rows(b["shq"], b["shs"]) - dequant_rows(ref["shared_hq"], ref["shared_hs"]))
+        dsh[~shared_dirty] = 0.0
+    tok_dirty = row_dirty[ref["dst_row"]].any(axis=1) | shared_dirty
+
+    yb = bf16_bits(y)
+    ulp = bf16_ulp_distance(yb, ref["y_bits"])
+    clean = ~tok_dirty
+    # clean tokens: 1 bf16 ulp, or (under cancellation) the GEMM tolerance of
+    # the magnitude sum of the terms that make up y
+    mag_y = np.zeros((T, H))
+    for k in range(K):
+        mag_y += ref["topk_gate"][:, k:k + 1].astype(np.float64) * ref["mag2"][ref["dst_row"][:, k]]
+    if shared is not None:
+        mag_y += ref["shared_mag2"]
+    yg = np_(y).astype(np.float64)
+    ok = (ulp <= 1) | (np.abs(yg - ref["y"]) <= 1e-4 * mag_y)
+    assert ok[clean].all(), f"clean tokens: {(~ok[clean]).sum()} elements beyond 1 ulp"
+    n_cancel = int(((ulp > 1) & clean[:, None]).sum())
+    n_dirty = int(tok_dirty.sum())
+    if n_dirty:
+        W2 = O.dequant_weight(w2q, w2s)
+        for t in np.nonzero(tok_dirty)[0]:
+            bound = np.zeros(H)
+            for k in range(K):
+                r = ref["dst_row"][t, k]
+                e = ref["topk_idx"][t, k]
+                bound += float(ref["topk_gate"][t, k]) * (np.abs(W2[e]) @ dh[r] + 1e-4 * ref["mag2"][r])
+            if dsh is not None:
+                SW2 = O.dequant_weight(shared[2], shared[3])[0]
+                bound += np.abs(SW2) @ dsh[t]
+            ulp_ref = np.spacing(np.abs(ref["y"][t]).astype(np.float32)).astype(np.float64) * 2 ** 16
+            assert np.all(np.abs(yg[t] - ref["y"][t]) <= ulp_ref + bound), t
+    return dict(dirty_tokens=n_dirty, tokens=T, h_code_diff_frac=frac, cancel_elems=n_cancel)
+
+
+@pytest.mark.parametrize("name", ["tiny", "tiny_sigmoid_shared", "small_moge"])
+@pytest.mark.parametrize("fused", [True, False])
+def test_layer_matches_oracle(name, fused):
+    cfg = _variant(name)
+    d, w, fwd, y = run_layer(cfg, fused)
+    stats = check_layer_against_oracle(cfg, d, w, fwd, y)
+    print(name, fused, stats)
+
+
+def test_layer_fused_equals_unfused_and_is_deterministic():
+    cfg = _variant("tiny_sigmoid_shared")
+    _, _, _, y1 = run_layer(cfg, True)
+    _, _, _, y2 = run_layer(cfg, False)
+    _, _, _, y3 = run_layer(cfg, True)
+    assert np.array_equal(bf16_bits(y1), bf16_bits(y2))
+    assert np.array_equal(bf16_bits(y1), bf16_bits(y3))
