@@ -8,37 +8,43 @@
 // Design:
 //  * The matrix core computes one whole 128-wide chunk per instruction
 //    (V_MFMA_F32_16X16X128_F8F6F4, 16x16 outputs, zero C input), so its
-//    float32 result is exactly the chunk partial P_kb.  The promotion is one
-//    VALU fused multiply-add per output per chunk:
-//    acc = fma(P_kb, sa * sb, acc), in chunk order.
-//  * The token dimension sits on the instruction's column axis and weight
-//    rows on its row axis: every lane's 4 outputs share one token (one sa per
-//    lane per chunk) and 4 consecutive weight rows inside one 128-row block
-//    (one sb per wave per chunk, a scalar load).
-//  * A workgroup owns a BM x BN tile of one group; 4 wavefronts each own a
-//    64 x 64 sub-tile (4 x 4 instruction tiles).  K advances one 128-byte
-//    chunk at a time through a double-buffered LDS stage filled with
-//    16-byte loads (8 lanes per 128-byte row segment, coalesced); rows are
-//    stored with a 16-byte XOR swizzle so the operand reads (32 bytes per
-//    lane) spread over the LDS banks.
+//    float32 result is the chunk partial P_kb.  The promotion is one VALU
+//    fused multiply-add per output per chunk: acc = fma(P_kb, sa * sb, acc),
+//    in chunk order.
+//  * Weight rows sit on the instruction's row axis and tokens on its column
+//    axis: each lane's 4 outputs share one token (one sa per lane per chunk)
+//    and 4 consecutive weight rows inside one 128-row block (one sb per wave
+//    per chunk, preloaded into LDS for the whole K range).
+//  * Workgroup tile: 256 weight rows x 128 tokens of one group, 8 wavefronts
+//    in a 4 (rows) x 2 (tokens) grid, each owning 64 x 64 outputs (4 x 4
+//    instruction tiles, 64 float32 accumulators per lane).
+//  * Memory pipeline: a 3-stage LDS ring filled by direct global->LDS loads
+//    (global_load_lds_dwordx4: no VGPR staging).  Each wave issues exactly
+//    7 loads per K step (2 activation, 4 weight, 1 activation-scale; past
+//    the end the last chunk is re-fetched so the count never varies), so
+//    "chunk kb has landed" is the wave's own s_waitcnt vmcnt(7) followed by a
+//    barrier; two chunks (~100 KB) stay in flight per CU while one is
+//    multiplied.  LDS rows are 128 bytes with a 16-byte XOR swizzle (applied
+//    on the global side, since the DMA fixes lane -> LDS address), so the
+//    32-byte operand reads spread over the banks.
 //  * Ragged groups: token rows past the group's end are clamped on load and
-//    never stored; 16-row instruction tiles that lie entirely past the end
-//    are skipped, so a group with M_g rows costs ceil(M_g / 16) tiles of
-//    matrix work, not BM.
+//    never stored; 16-row instruction tiles past the end are skipped, so a
+//    group of M_g rows costs ceil(M_g / 16) tiles of matrix work.
 //  * Tile table on the device, no host sync: every workgroup reads the group
-//    offsets, counts each group's m-tiles, prefix-sums them in LDS and finds
-//    its own tile, so the grid is sized from the host-known bound
-//    floor(M / BM) + G m-tiles.
+//    offsets, prefix-sums the m-tile counts in LDS (scratch aliased onto the
+//    ring) and locates its own tile; the grid is sized from the host-known
+//    bound floor(M / BM) + G m-tiles and surplus workgroups exit.
 //  * XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so
-//    block b is remapped to logical tile xcd * ceil(tiles / 8) + b / 8.  Each
-//    XCD then sweeps a contiguous run of (group, n-tile, m-tile) tiles:
-//    m-tiles sharing one weight slab and n-tiles sharing one activation tile
-//    run together on one XCD and share its L2.
-//  * Fused SwiGLU (grouped_gemm_fp8_swiglu): the B tile is the gate block c
-//    (weight rows 128c..) stacked on the up block c (rows I + 128c..), and
-//    every wave holds matching gate and up rows, so h = silu(g) * u is formed
-//    in registers; the 1x128 amax of h along I is reduced across lanes and
-//    waves through LDS, and only the FP8 codes and scales of h are written.
+//    block b works on logical tile (b % 8) * ceil(tiles / 8) + b / 8.  Each
+//    XCD sweeps a contiguous run of (group, n-tile, m-tile) tiles: the
+//    m-tiles of one weight slab and the n-tiles of one activation tile run
+//    together on one XCD and share its L2, so each weight byte crosses HBM
+//    about once.
+//  * Fused SwiGLU (grouped_gemm_fp8_swiglu): the weight tile is gate block c
+//    (rows 128c..) stacked on up block c (rows I + 128c..); each wave holds
+//    matching gate and up rows, so h = silu(g) * u forms in registers, the
+//    1x128 amax of h along I is reduced across lanes and the 4 row-waves
+//    through LDS, and only h's FP8 codes and scales are written.
 #include "device_common.h"
 #include "host_common.h"
 
@@ -50,8 +56,38 @@ typedef float v4f __attribute__((ext_vector_type(4)));
 
 enum { OUT_F32 = 0, OUT_BF16 = 1, OUT_SWIGLU = 2 };
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;          // 8 wavefronts
+constexpr int kBN = 256;               // weight rows per workgroup tile
+constexpr int kBM = 128;               // tokens per workgroup tile
+constexpr int kStages = 3;
 constexpr int kMaxGroups = 1024;
+constexpr int kMaxKB = 512;            // K <= 65536
+constexpr int kOffA = 0;                         // [128 rows][128 B]
+constexpr int kOffB = kBM * 128;                 // [256 rows][128 B]
+constexpr int kOffSA = kOffB + kBN * 128;        // [8 waves][64] float
+constexpr int kStageBytes = kOffSA + 8 * 64 * 4;  // 51200
+constexpr int kDmaPerChunk = 7;                  // per wave: 2 A + 4 B + 1 scale
+
+// LDS byte address of a __shared__ location.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
+}
+
+// Direct global -> LDS loads (gfx950 global_load_lds_dword[x4]): lane i's
+// 16 (4) bytes land at LDS address `lds` + 16 i (4 i).  Issued from inline
+// assembly so that the compiler's wait-count pass does not track them: its
+// alias tracking of LDS DMA is coarse and would otherwise force every LDS
+// read in the K loop to wait for ALL outstanding DMA, serialising the ring.
+// The kernel waits for these loads itself (s_waitcnt vmcnt + s_barrier), and
+// no compiler-visible vector loads are in flight while they are.  The
+// instructions have no destination registers; the address VGPRs are read at
+// issue.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds), "v"(g) : "memory", "m0");
+}
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" : : "s"(lds), "v"(g) : "memory", "m0");
+}
 
 __device__ __forceinline__ v4f mfma_chunk(const v8i& a, const v8i& b) {
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
@@ -59,59 +95,54 @@ __device__ __forceinline__ v4f mfma_chunk(const v8i& a, const v8i& b) {
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
 }
 
-// Byte offset of 16-byte piece c16 of row r inside a [rows][128] LDS stage.
+// Byte offset of logical 16-byte piece c16 of row r inside a [rows][128 B] tile.
 __device__ __forceinline__ int swz(int r, int c16) { return r * 128 + ((c16 ^ (r & 7)) << 4); }
 
-// 32 bytes of row r starting at byte 32 * q (q = lane / 16) -> v8i.
-__device__ __forceinline__ v8i lds_operand(const uint8_t* stage, int r, int q) {
-  const u32x4 lo = *reinterpret_cast<const u32x4*>(stage + swz(r, 2 * q));
-  const u32x4 hi = *reinterpret_cast<const u32x4*>(stage + swz(r, 2 * q + 1));
+// 32 bytes of row r starting at logical byte 32 * q (q = lane / 16) -> v8i.
+__device__ __forceinline__ v8i lds_operand(const uint8_t* tile, int r, int q) {
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(tile + swz(r, 2 * q));
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(tile + swz(r, 2 * q + 1));
   v8i v;
   v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
   v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
   return v;
 }
 
-template <int BM, int BN, int WM, int WN, int MODE>
-__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
+template <int MODE>
+__global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
     const uint8_t* __restrict__ aq, const float* __restrict__ as, const uint8_t* __restrict__ bq,
     const float* __restrict__ bs, const int* __restrict__ offsets, int G, int N, int K, int n_tiles,
     void* __restrict__ out, float* __restrict__ hs_out) {
-  static_assert(WM * WN == 4, "4 wavefronts");
-  constexpr int WTM = BM / WM;     // tokens per wave
-  constexpr int WTN = BN / WN;     // weight rows per wave
-  constexpr int NTM = WTM / 16;    // instruction tiles along tokens
-  constexpr int NTN = WTN / 16;    // instruction tiles along weight rows
   constexpr bool kFused = MODE == OUT_SWIGLU;
-  static_assert(!kFused || BN == 256, "fused tile = 128 gate rows + 128 up rows");
-  static_assert(kFused || WTN <= 128, "a wave's rows must sit in one 128-row block");
-  constexpr int APT = BM * 8 / kThreads;  // 16-byte A pieces per thread per chunk
-  constexpr int BPT = BN * 8 / kThreads;  // 16-byte B pieces per thread per chunk
-  static_assert(APT >= 1 && BPT >= 1, "tile too small");
-
-  __shared__ __attribute__((aligned(16))) uint8_t sA[2][BM * 128];
-  __shared__ __attribute__((aligned(16))) uint8_t sB[2][BN * 128];
-  __shared__ float sSA[2][BM];
-  __shared__ int sP[kMaxGroups + 1];
-  __shared__ int sOff[kMaxGroups + 1];
-  __shared__ int sScan[kThreads];
-  __shared__ float sAmax[kFused ? WN : 1][kFused ? BM : 1];
+  // three ring stages as separate LDS objects: the compiler can then tell a
+  // DMA into one stage from reads of another and adds no extra waits
+  __shared__ __attribute__((aligned(1024))) uint8_t ring0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring2[kStageBytes];
+  __shared__ float sSB[2][kMaxKB];
+  __shared__ float sAmax[kFused ? 4 : 1][kFused ? kBM : 1];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) wave index
+  const int wn = w & 3, wm = w >> 2;
+  const int q = lane >> 4, l16 = lane & 15;
 
-  // ---- tile table: m-tiles per group, prefix sums, this block's tile ----
+  // ---- tile table (LDS scratch aliased onto the ring) ----
+  int* sP = reinterpret_cast<int*>(ring0);                // [G + 1]
+  int* sOff = sP + (kMaxGroups + 1);                      // [G + 1]
+  int* sScan = sOff + (kMaxGroups + 1);                   // [kThreads]
   {
+    int mt[2];
     int local = 0;
-    int mt[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int g = tid * 4 + i;
+    for (int i = 0; i < 2; ++i) {
+      const int g = tid * 2 + i;
       mt[i] = 0;
       if (g < G) {
         const int o0 = offsets[g], o1 = offsets[g + 1];
         sOff[g] = o0;
-        mt[i] = (o1 - o0 + BM - 1) / BM;
+        mt[i] = (o1 - o0 + kBM - 1) / kBM;
         if (g == G - 1) sOff[G] = o1;
       }
       local += mt[i];
@@ -126,20 +157,19 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     }
     int run = sScan[tid] - local;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int g = tid * 4 + i;
+    for (int i = 0; i < 2; ++i) {
+      const int g = tid * 2 + i;
       if (g < G) sP[g] = run;
       run += mt[i];
     }
     if (tid == kThreads - 1) sP[G] = sScan[kThreads - 1];
     __syncthreads();
   }
-  const int total_mt = sP[G];
-  const int total = total_mt * n_tiles;
-  const int chunk = (total + 7) / 8;
+  const int total = sP[G] * n_tiles;
+  const int per_xcd = (total + 7) / 8;
   const int slot = blockIdx.x >> 3;
-  if (slot >= chunk) return;
-  const int lid = (blockIdx.x & 7) * chunk + slot;
+  if (slot >= per_xcd) return;
+  const int lid = (blockIdx.x & 7) * per_xcd + slot;
   if (lid >= total) return;
   int g;
   {
@@ -154,111 +184,103 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   const int local_id = lid - sP[g] * n_tiles;
   const int n_tile = local_id / mt_g;
   const int m_tile = local_id % mt_g;
-  const int row0 = sOff[g] + m_tile * BM;
-  const int rows_valid = min(BM, sOff[g + 1] - row0);
+  const int row0 = sOff[g] + m_tile * kBM;
+  const int rows_valid = min(kBM, sOff[g + 1] - row0);
   const int KB = K / 128;
-  const int I = N / 2;  // fused mode: gate rows [0, I), up rows [I, 2I)
-
-  const int wn = wave % WN, wm = wave / WN;
-  // 128-row weight blocks of this wave's rows (gate / up blocks in fused mode)
-  const int blk0 = kFused ? n_tile : (n_tile * BN + wn * WTN) / 128;
-  const int blk1 = kFused ? I / 128 + n_tile : blk0;
-
+  const int I = N / 2;  // fused: gate rows [0, I), up rows [I, 2I)
   const uint8_t* bq_g = bq + (int64_t)g * N * K;
   const float* bs_g = bs + (int64_t)g * (N / 128) * KB;
-
-  // ---- global -> register staging of one chunk (fully unrolled) ----
-  u32x4 ra[APT], rb[BPT];
-  float rsa = 0.f;
-  float rsb0 = 0.f, rsb1 = 0.f;  // weight-block scales of the staged chunk (wave-uniform)
-  const uint8_t* a_src[APT];      // per-piece row base pointers (chunk 0)
-  const uint8_t* b_src[BPT];
-#pragma unroll
-  for (int i = 0; i < APT; ++i) {
-    const int p = i * kThreads + tid;
-    const int64_t grow = row0 + min(p >> 3, rows_valid - 1);
-    a_src[i] = aq + grow * K + (p & 7) * 16;
+  // the two 128-row weight blocks of this tile
+  const int nblk = N / 128;
+  const int blkA = kFused ? n_tile : 2 * n_tile;
+  const int blkB = kFused ? I / 128 + n_tile : min(2 * n_tile + 1, nblk - 1);
+  __syncthreads();  // tile-table scratch is about to be overwritten
+  for (int i = tid; i < KB; i += kThreads) {
+    sSB[0][i] = bs_g[(int64_t)blkA * KB + i];
+    sSB[1][i] = bs_g[(int64_t)blkB * KB + i];
   }
-#pragma unroll
-  for (int i = 0; i < BPT; ++i) {
-    const int p = i * kThreads + tid;
-    const int r = p >> 3;
-    const int wrow = kFused ? (r < 128 ? n_tile * 128 + r : I + n_tile * 128 + (r - 128))
-                            : n_tile * BN + r;
-    b_src[i] = bq_g + (int64_t)wrow * K + (p & 7) * 16;
-  }
-  const float* sa_src = as + (int64_t)(row0 + min(tid, rows_valid - 1)) * KB;
-  const float* sb_src0 = bs_g + (int64_t)blk0 * KB;
-  const float* sb_src1 = bs_g + (int64_t)blk1 * KB;
 
-#define MOE_LOAD_CHUNK(kb)                                                        \
-  do {                                                                            \
-    _Pragma("unroll") for (int i = 0; i < APT; ++i) ra[i] =                       \
-        *reinterpret_cast<const u32x4*>(a_src[i] + (kb) * 128);                   \
-    _Pragma("unroll") for (int i = 0; i < BPT; ++i) rb[i] =                       \
-        *reinterpret_cast<const u32x4*>(b_src[i] + (kb) * 128);                   \
-    if (tid < BM) rsa = sa_src[kb];                                               \
-    rsb0 = sb_src0[kb];                                                           \
-    rsb1 = sb_src1[kb];                                                           \
-  } while (0)
-#define MOE_STORE_CHUNK(s)                                                        \
-  do {                                                                            \
-    _Pragma("unroll") for (int i = 0; i < APT; ++i) {                             \
-      const int p = i * kThreads + tid;                                           \
-      *reinterpret_cast<u32x4*>(&sA[s][swz(p >> 3, p & 7)]) = ra[i];              \
-    }                                                                             \
-    _Pragma("unroll") for (int i = 0; i < BPT; ++i) {                             \
-      const int p = i * kThreads + tid;                                           \
-      *reinterpret_cast<u32x4*>(&sB[s][swz(p >> 3, p & 7)]) = rb[i];              \
-    }                                                                             \
-    if (tid < BM) sSA[s][tid] = rsa;                                              \
-  } while (0)
+  // ---- per-lane global row pointers of this wave's DMA slices ----
+  const int p16 = lane & 7;           // physical 16-byte piece inside the LDS row
+  const int rsub = lane >> 3;         // row inside the 8-row (1 KB) DMA slice
+  const int c16 = p16 ^ rsub;         // logical piece it must fetch (swizzle)
+  const uint8_t* a_src[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = (w * 2 + i) * 8 + rsub;
+    a_src[i] = aq + (int64_t)(row0 + min(r, rows_valid - 1)) * K + c16 * 16;
+  }
+  const uint8_t* b_src[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = (w * 4 + i) * 8 + rsub;
+    int wrow;
+    if (kFused) wrow = r < 128 ? n_tile * 128 + r : I + n_tile * 128 + (r - 128);
+    else wrow = min(n_tile * kBN + r, N - 1);
+    b_src[i] = bq_g + (int64_t)wrow * K + c16 * 16;
+  }
+  const float* sa_src = as + (int64_t)(row0 + min(wm * 64 + lane, rows_valid - 1)) * KB;
+
+  auto issue = [&](int kb, uint8_t* st) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(st));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma16(a_src[i] + kb * 128, base + kOffA + (w * 2 + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma16(b_src[i] + kb * 128, base + kOffB + (w * 4 + i) * 1024);
+    dma4(sa_src + kb, base + kOffSA + w * 256);
+  };
 
   // ---- wave geometry ----
-  const int q = lane >> 4, l16 = lane & 15;
-  int brow[NTN];  // B-tile row of n-tile i for this lane
+  int brow[4];  // row of n-tile i inside the weight tile, for this lane
 #pragma unroll
-  for (int i = 0; i < NTN; ++i) {
-    if (kFused) {
-      constexpr int half = NTN / 2;
-      brow[i] = (i < half ? 0 : 128) + wn * (128 / WN) + 16 * (i % half) + l16;
-    } else {
-      brow[i] = wn * WTN + 16 * i + l16;
-    }
-  }
-  int n_active = 0;  // instruction tiles along tokens holding a valid row
+  for (int i = 0; i < 4; ++i)
+    brow[i] = kFused ? (i < 2 ? 0 : 128) + 32 * wn + 16 * (i & 1) + l16 : 64 * wn + 16 * i + l16;
+  int n_active = 0;
 #pragma unroll
-  for (int j = 0; j < NTM; ++j)
-    if (wm * WTM + 16 * j < rows_valid) n_active = j + 1;
+  for (int j = 0; j < 4; ++j)
+    if (wm * 64 + 16 * j < rows_valid) n_active = j + 1;
+  const bool wave_rows_valid = kFused || (n_tile * kBN + wn * 64 < N);
+  if (!wave_rows_valid) n_active = 0;
+  const int sb_sel = kFused ? 0 : (wn >> 1);  // unfused: rows of waves 0,1 in block A, 2,3 in B
 
-  v4f acc[NTN][NTM];
+  v4f acc[4][4];
 #pragma unroll
-  for (int i = 0; i < NTN; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < NTM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  MOE_LOAD_CHUNK(0);
-  float sb0 = rsb0, sb1 = rsb1;
-  MOE_STORE_CHUNK(0);
-  __syncthreads();
-  for (int kb = 0; kb < KB; ++kb) {
-    const int s = kb & 1;
-    if (kb + 1 < KB) MOE_LOAD_CHUNK(kb + 1);
-    v8i a_op[NTN];
+  __syncthreads();  // sSB visible; no loads are in flight yet
+  // Every step issues exactly kDmaPerChunk loads, so "chunk kb has landed" is
+  // always vmcnt(kDmaPerChunk): past the end the last chunk is re-fetched (an
+  // L2 hit) into the free stage instead of issuing nothing.
+  issue(0, ring0);
+  issue(min(1, KB - 1), ring1);
+
+  // One K step on the stage holding chunk kb; `nxt` receives chunk kb + 2.
+  auto step = [&](int kb, const uint8_t* st, uint8_t* nxt) {
+    // this wave's loads of chunk kb have landed (only chunk kb+1's may still fly) ...
+    __builtin_amdgcn_s_waitcnt(0x0F70 | kDmaPerChunk);
+    // ... and every other wave's too; all waves are also done with chunk kb-1,
+    // whose stage `nxt` is refilled now
+    __builtin_amdgcn_s_barrier();
+    issue(min(kb + 2, KB - 1), nxt);
+    const float* sSA = reinterpret_cast<const float*>(st + kOffSA) + w * 64;
+    v8i a_op[4];
 #pragma unroll
-    for (int i = 0; i < NTN; ++i) a_op[i] = lds_operand(sB[s], brow[i], q);
+    for (int i = 0; i < 4; ++i) a_op[i] = lds_operand(st + kOffB, brow[i], q);
+    const float sb0 = kFused ? sSB[0][kb] : sSB[sb_sel][kb];
+    const float sb1 = kFused ? sSB[1][kb] : sb0;
 #pragma unroll
-    for (int j = 0; j < NTM; ++j) {
+    for (int j = 0; j < 4; ++j) {
       if (j < n_active) {
-        const int arow = wm * WTM + 16 * j + l16;
-        const v8i b_op = lds_operand(sA[s], arow, q);
-        const float sa = sSA[s][arow];
+        const v8i b_op = lds_operand(st + kOffA, wm * 64 + 16 * j + l16, q);
+        const float sa = sSA[16 * j + l16];
         const float sc0 = sa * sb0;
         const float sc1 = kFused ? sa * sb1 : sc0;
 #pragma unroll
-        for (int i = 0; i < NTN; ++i) {
+        for (int i = 0; i < 4; ++i) {
           const v4f p = mfma_chunk(a_op[i], b_op);
-          const float sc = (kFused && i >= NTN / 2) ? sc1 : sc0;
+          const float sc = (kFused && i >= 2) ? sc1 : sc0;
           acc[i][j][0] = __builtin_fmaf(p[0], sc, acc[i][j][0]);
           acc[i][j][1] = __builtin_fmaf(p[1], sc, acc[i][j][1]);
           acc[i][j][2] = __builtin_fmaf(p[2], sc, acc[i][j][2]);
@@ -266,27 +288,24 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
         }
       }
     }
-    if (kb + 1 < KB) {
-      MOE_STORE_CHUNK(s ^ 1);
-      sb0 = rsb0;
-      sb1 = rsb1;
-    }
-    __syncthreads();
+  };
+  for (int kb = 0; kb < KB; kb += 3) {
+    step(kb, ring0, ring2);
+    if (kb + 1 < KB) step(kb + 1, ring1, ring0);
+    if (kb + 2 < KB) step(kb + 2, ring2, ring1);
   }
-
-#undef MOE_LOAD_CHUNK
-#undef MOE_STORE_CHUNK
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // drain the trailing re-fetches
 
   // ---- epilogue ----
   if constexpr (!kFused) {
 #pragma unroll
-    for (int j = 0; j < NTM; ++j) {
-      const int mloc = wm * WTM + 16 * j + l16;
+    for (int j = 0; j < 4; ++j) {
+      const int mloc = wm * 64 + 16 * j + l16;
       if (j < n_active && mloc < rows_valid) {
         const int64_t m = row0 + mloc;
 #pragma unroll
-        for (int i = 0; i < NTN; ++i) {
-          const int n = n_tile * BN + wn * WTN + 16 * i + 4 * q;
+        for (int i = 0; i < 4; ++i) {
+          const int n = n_tile * kBN + wn * 64 + 16 * i + 4 * q;
           if (MODE == OUT_F32) {
             float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
             *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + m * N + n) = v;
@@ -300,61 +319,58 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
       }
     }
   } else {
-    constexpr int HALF = NTN / 2;
-    // h = silu(g) * u into the gate accumulators; per-token amax
+    // h = silu(g) * u into the gate accumulators; per-token amax over this
+    // wave's 32 h columns, then across the 4 row-waves through LDS
 #pragma unroll
-    for (int j = 0; j < NTM; ++j) {
+    for (int j = 0; j < 4; ++j) {
       float amax = 0.f;
 #pragma unroll
-      for (int i = 0; i < HALF; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float h = spec_silu(acc[i][j][v]) * acc[i + HALF][j][v];
+          const float h = spec_silu(acc[i][j][v]) * acc[i + 2][j][v];
           acc[i][j][v] = h;
           amax = fmaxf(amax, fabsf(h));
         }
       amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
       amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-      if (q == 0) sAmax[wn][wm * WTM + 16 * j + l16] = amax;
+      if (q == 0) sAmax[wn][wm * 64 + 16 * j + l16] = amax;
     }
     __syncthreads();
-    const int Ih = I;  // h row length
+    uint8_t* hq = reinterpret_cast<uint8_t*>(out);
 #pragma unroll
-    for (int j = 0; j < NTM; ++j) {
-      const int mloc = wm * WTM + 16 * j + l16;
+    for (int j = 0; j < 4; ++j) {
+      const int mloc = wm * 64 + 16 * j + l16;
       if (j < n_active && mloc < rows_valid) {
-        float amax = 0.f;
-#pragma unroll
-        for (int w = 0; w < WN; ++w) amax = fmaxf(amax, sAmax[w][mloc]);
+        const float amax = fmaxf(fmaxf(sAmax[0][mloc], sAmax[1][mloc]), fmaxf(sAmax[2][mloc], sAmax[3][mloc]));
         const float sc = scale_from_amax(amax);
         const int64_t m = row0 + mloc;
-        uint8_t* hq = reinterpret_cast<uint8_t*>(out);
 #pragma unroll
-        for (int i = 0; i < HALF; ++i) {
-          const int col = n_tile * 128 + wn * (128 / WN) + 16 * i + 4 * q;
-          const uint32_t w = quantize(acc[i][j][0], sc) | (quantize(acc[i][j][1], sc) << 8) |
-                             (quantize(acc[i][j][2], sc) << 16) | (quantize(acc[i][j][3], sc) << 24);
-          *reinterpret_cast<uint32_t*>(hq + m * Ih + col) = w;
+        for (int i = 0; i < 2; ++i) {
+          const int col = n_tile * 128 + 32 * wn + 16 * i + 4 * q;
+          const uint32_t wd = quantize(acc[i][j][0], sc) | (quantize(acc[i][j][1], sc) << 8) |
+                              (quantize(acc[i][j][2], sc) << 16) | (quantize(acc[i][j][3], sc) << 24);
+          *reinterpret_cast<uint32_t*>(hq + m * I + col) = wd;
         }
-        if (wn == 0 && q == 0) hs_out[m * (Ih / 128) + n_tile] = sc;
+        if (wn == 0 && q == 0) hs_out[m * (I / 128) + n_tile] = sc;
       }
     }
   }
 }
 
-template <int BM, int BN, int WM, int WN, int MODE>
+template <int MODE>
 moe_status launch_gemm(const uint8_t* aq, const float* as, const uint8_t* bq, const float* bs,
                        const int* offsets, int G, int64_t M, int N, int K, void* out, float* hs,
                        hipStream_t st, const char* what) {
-  const int n_tiles = MODE == OUT_SWIGLU ? (N / 2) / 128 : N / BN;
-  int64_t mt_bound = M / BM + G;
+  const int n_tiles = MODE == OUT_SWIGLU ? (N / 2) / 128 : (N + kBN - 1) / kBN;
+  int64_t mt_bound = M / kBM + G;
   if (mt_bound > M) mt_bound = M;
   const int64_t tiles = mt_bound * n_tiles;
   const int64_t grid = (tiles + 7) / 8 * 8;
   if (grid >= (1LL << 31)) return fail(MOE_ERR_UNSUPPORTED, "%s: too many tiles", what);
   if (grid == 0) return MOE_OK;
-  grouped_gemm_kernel<BM, BN, WM, WN, MODE>
-      <<<(unsigned)grid, kThreads, 0, st>>>(aq, as, bq, bs, offsets, G, N, K, n_tiles, out, hs);
+  grouped_gemm_kernel<MODE><<<(unsigned)grid, kThreads, 0, st>>>(aq, as, bq, bs, offsets, G, N, K, n_tiles,
+                                                                 out, hs);
   return after_launch(what, st);
 }
 
@@ -364,6 +380,7 @@ moe_status check_gemm_args(const uint8_t* aq, const float* as, const uint8_t* bq
               (long long)M, N, K);
   MOE_REQUIRE(G <= kMaxGroups, MOE_ERR_UNSUPPORTED, "G=%d > %d", G, kMaxGroups);
   MOE_REQUIRE(N % 128 == 0 && K % 128 == 0, MOE_ERR_SHAPE, "N=%d and K=%d must be multiples of 128", N, K);
+  MOE_REQUIRE(K <= 128 * kMaxKB, MOE_ERR_UNSUPPORTED, "K=%d > %d", K, 128 * kMaxKB);
   MOE_REQUIRE(M < (1LL << 31), MOE_ERR_UNSUPPORTED, "M too large");
   MOE_REQUIRE(offsets, MOE_ERR_NULL, "group_offsets is required");
   MOE_REQUIRE(aligned(offsets, 4), MOE_ERR_ALIGN, "group_offsets needs 4-byte alignment");
@@ -392,10 +409,10 @@ extern "C" moe_status grouped_gemm_fp8_blockscaled(const uint8_t* aq, const floa
   MOE_REQUIRE(aligned(c, 16), MOE_ERR_ALIGN, "c needs 16-byte alignment");
   hipStream_t st = as_stream(stream);
   if (c_dtype == MOE_F32)
-    return launch_gemm<128, 128, 2, 2, OUT_F32>(aq, as, bq, bs, group_offsets, G, M, N, K, c, nullptr,
-                                                st, "grouped_gemm_fp8_blockscaled");
-  return launch_gemm<128, 128, 2, 2, OUT_BF16>(aq, as, bq, bs, group_offsets, G, M, N, K, c, nullptr,
-                                               st, "grouped_gemm_fp8_blockscaled");
+    return launch_gemm<OUT_F32>(aq, as, bq, bs, group_offsets, G, M, N, K, c, nullptr, st,
+                                "grouped_gemm_fp8_blockscaled");
+  return launch_gemm<OUT_BF16>(aq, as, bq, bs, group_offsets, G, M, N, K, c, nullptr, st,
+                               "grouped_gemm_fp8_blockscaled");
 }
 
 extern "C" moe_status grouped_gemm_fp8_swiglu(const uint8_t* aq, const float* as, const uint8_t* bq,
@@ -409,6 +426,6 @@ extern "C" moe_status grouped_gemm_fp8_swiglu(const uint8_t* aq, const float* as
   MOE_REQUIRE(hq && hs, MOE_ERR_NULL, "hq and hs are required");
   MOE_REQUIRE(aligned(hq, 16) && aligned(hs, 4), MOE_ERR_ALIGN, "hq needs 16-byte alignment");
   hipStream_t st = as_stream(stream);
-  return launch_gemm<64, 256, 1, 4, OUT_SWIGLU>(aq, as, bq, bs, group_offsets, G, M, 2 * I, K, hq, hs, st,
-                                                "grouped_gemm_fp8_swiglu");
+  return launch_gemm<OUT_SWIGLU>(aq, as, bq, bs, group_offsets, G, M, 2 * I, K, hq, hs, st,
+                                 "grouped_gemm_fp8_swiglu");
 }
