@@ -14,16 +14,20 @@
 //  * Weight rows sit on the instruction's row axis and tokens on its column
 //    axis: each lane's 4 outputs share one token (one sa per lane per chunk)
 //    and 4 consecutive weight rows inside one 128-row block (one sb per wave
-//    per chunk, preloaded into LDS for the whole K range).
-//  * Workgroup tile: 256 weight rows x 128 tokens of one group, 8 wavefronts
-//    in a 4 (rows) x 2 (tokens) grid, each owning 64 x 64 outputs (4 x 4
-//    instruction tiles, 64 float32 accumulators per lane).
+//    per chunk).
+//  * Workgroup tile: 256 weight rows x 160 tokens of one group, 8 wavefronts
+//    in a 4 (rows) x 2 (tokens) grid, each owning 64 x 80 outputs (4 x 5
+//    instruction tiles, 80 float32 accumulators per lane).  160 tokens, not
+//    128: a group slightly above the mean load (the usual case with top-K
+//    routing) still fits one m-tile, so its weights are streamed once.
 //  * Memory pipeline: a 3-stage LDS ring filled by direct global->LDS loads
 //    (global_load_lds_dwordx4: no VGPR staging).  Each wave issues exactly
-//    7 loads per K step (2 activation, 4 weight, 1 activation-scale; past
-//    the end the last chunk is re-fetched so the count never varies), so
-//    "chunk kb has landed" is the wave's own s_waitcnt vmcnt(7) followed by a
-//    barrier; two chunks (~100 KB) stay in flight per CU while one is
+//    7 loads per K step (waves 0-3: 3 activation + 4 weight slices; waves
+//    4-7: 2 activation + 4 weight slices + 1 scale load, which carries the
+//    activation scales or, in wave 7, the two weight-block scales; past the
+//    end the last chunk is re-fetched so the count never varies), so "chunk
+//    kb has landed" is the wave's own s_waitcnt vmcnt(7) followed by a
+//    barrier; two chunks (~106 KB) stay in flight per CU while one is
 //    multiplied.  LDS rows are 128 bytes with a 16-byte XOR swizzle (applied
 //    on the global side, since the DMA fixes lane -> LDS address), so the
 //    32-byte operand reads spread over the banks.
@@ -58,15 +62,18 @@ enum { OUT_F32 = 0, OUT_BF16 = 1, OUT_SWIGLU = 2 };
 
 constexpr int kThreads = 512;          // 8 wavefronts
 constexpr int kBN = 256;               // weight rows per workgroup tile
-constexpr int kBM = 128;               // tokens per workgroup tile
+constexpr int kBM = 160;               // tokens per workgroup tile
+constexpr int kWM = kBM / 2;           // tokens per wavefront
+constexpr int kTM = kWM / 16;          // 16-token instruction tiles per wavefront
 constexpr int kStages = 3;
 constexpr int kMaxGroups = 1024;
 constexpr int kMaxKB = 512;            // K <= 65536
-constexpr int kOffA = 0;                         // [128 rows][128 B]
+constexpr int kOffA = 0;                         // [160 rows][128 B]
 constexpr int kOffB = kBM * 128;                 // [256 rows][128 B]
-constexpr int kOffSA = kOffB + kBN * 128;        // [8 waves][64] float
-constexpr int kStageBytes = kOffSA + 8 * 64 * 4;  // 51200
-constexpr int kDmaPerChunk = 7;                  // per wave: 2 A + 4 B + 1 scale
+constexpr int kOffS = kOffB + kBN * 128;         // [256] float: 192 activation scales, 2 weight scales
+constexpr int kSB = 192;                         // float index of the weight-block scales in S
+constexpr int kStageBytes = kOffS + 4 * 64 * 4;  // 54272; 3 stages = 162816 B of LDS
+constexpr int kDmaPerChunk = 7;                  // per wave, see the memory pipeline notes
 
 // LDS byte address of a __shared__ location.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -119,8 +126,6 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
   __shared__ __attribute__((aligned(1024))) uint8_t ring0[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t ring1[kStageBytes];
   __shared__ __attribute__((aligned(1024))) uint8_t ring2[kStageBytes];
-  __shared__ float sSB[2][kMaxKB];
-  __shared__ float sAmax[kFused ? 4 : 1][kFused ? kBM : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -194,20 +199,18 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
   const int nblk = N / 128;
   const int blkA = kFused ? n_tile : 2 * n_tile;
   const int blkB = kFused ? I / 128 + n_tile : min(2 * n_tile + 1, nblk - 1);
-  __syncthreads();  // tile-table scratch is about to be overwritten
-  for (int i = tid; i < KB; i += kThreads) {
-    sSB[0][i] = bs_g[(int64_t)blkA * KB + i];
-    sSB[1][i] = bs_g[(int64_t)blkB * KB + i];
-  }
 
   // ---- per-lane global row pointers of this wave's DMA slices ----
   const int p16 = lane & 7;           // physical 16-byte piece inside the LDS row
   const int rsub = lane >> 3;         // row inside the 8-row (1 KB) DMA slice
   const int c16 = p16 ^ rsub;         // logical piece it must fetch (swizzle)
-  const uint8_t* a_src[2];
+  // activation slices (8 rows each): waves 0-3 take 3, waves 4-7 take 2
+  const bool a3 = w < 4;
+  const int a_slice0 = a3 ? 3 * w : 12 + 2 * (w - 4);
+  const uint8_t* a_src[3];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int r = (w * 2 + i) * 8 + rsub;
+  for (int i = 0; i < 3; ++i) {
+    const int r = (a_slice0 + i) * 8 + rsub;
     a_src[i] = aq + (int64_t)(row0 + min(r, rows_valid - 1)) * K + c16 * 16;
   }
   const uint8_t* b_src[4];
@@ -219,15 +222,21 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
     else wrow = min(n_tile * kBN + r, N - 1);
     b_src[i] = bq_g + (int64_t)wrow * K + c16 * 16;
   }
-  const float* sa_src = as + (int64_t)(row0 + min(wm * 64 + lane, rows_valid - 1)) * KB;
+  // scale loads (waves 4-7): S[t] = sa of token t for t < 192 (rows past the
+  // group clamped), S[192] / S[193] = the scales of weight blocks A / B
+  const float* s_src = as;
+  if (w >= 4 && w < 7) s_src = as + (int64_t)(row0 + min((w - 4) * 64 + lane, rows_valid - 1)) * KB;
+  else s_src = bs_g + (int64_t)(lane == 0 ? blkA : blkB) * KB;
+  __syncthreads();  // tile-table scratch (aliased onto ring0) is about to be overwritten
 
   auto issue = [&](int kb, uint8_t* st) {
     const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(st));
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(a_src[i] + kb * 128, base + kOffA + (w * 2 + i) * 1024);
+    for (int i = 0; i < 2; ++i) dma16(a_src[i] + kb * 128, base + kOffA + (a_slice0 + i) * 1024);
+    if (a3) dma16(a_src[2] + kb * 128, base + kOffA + (a_slice0 + 2) * 1024);
+    else dma4(s_src + kb, base + kOffS + (w - 4) * 256);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dma16(b_src[i] + kb * 128, base + kOffB + (w * 4 + i) * 1024);
-    dma4(sa_src + kb, base + kOffSA + w * 256);
   };
 
   // ---- wave geometry ----
@@ -237,19 +246,18 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
     brow[i] = kFused ? (i < 2 ? 0 : 128) + 32 * wn + 16 * (i & 1) + l16 : 64 * wn + 16 * i + l16;
   int n_active = 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    if (wm * 64 + 16 * j < rows_valid) n_active = j + 1;
+  for (int j = 0; j < kTM; ++j)
+    if (wm * kWM + 16 * j < rows_valid) n_active = j + 1;
   const bool wave_rows_valid = kFused || (n_tile * kBN + wn * 64 < N);
   if (!wave_rows_valid) n_active = 0;
   const int sb_sel = kFused ? 0 : (wn >> 1);  // unfused: rows of waves 0,1 in block A, 2,3 in B
 
-  v4f acc[4][4];
+  v4f acc[4][kTM];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kTM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  __syncthreads();  // sSB visible; no loads are in flight yet
   // Every step issues exactly kDmaPerChunk loads, so "chunk kb has landed" is
   // always vmcnt(kDmaPerChunk): past the end the last chunk is re-fetched (an
   // L2 hit) into the free stage instead of issuing nothing.
@@ -264,17 +272,17 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
     // whose stage `nxt` is refilled now
     __builtin_amdgcn_s_barrier();
     issue(min(kb + 2, KB - 1), nxt);
-    const float* sSA = reinterpret_cast<const float*>(st + kOffSA) + w * 64;
+    const float* sS = reinterpret_cast<const float*>(st + kOffS);
     v8i a_op[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) a_op[i] = lds_operand(st + kOffB, brow[i], q);
-    const float sb0 = kFused ? sSB[0][kb] : sSB[sb_sel][kb];
-    const float sb1 = kFused ? sSB[1][kb] : sb0;
+    const float sb0 = kFused ? sS[kSB] : sS[kSB + sb_sel];
+    const float sb1 = kFused ? sS[kSB + 1] : sb0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kTM; ++j) {
       if (j < n_active) {
-        const v8i b_op = lds_operand(st + kOffA, wm * 64 + 16 * j + l16, q);
-        const float sa = sSA[16 * j + l16];
+        const v8i b_op = lds_operand(st + kOffA, wm * kWM + 16 * j + l16, q);
+        const float sa = sS[wm * kWM + 16 * j + l16];
         const float sc0 = sa * sb0;
         const float sc1 = kFused ? sa * sb1 : sc0;
 #pragma unroll
@@ -299,8 +307,8 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
   // ---- epilogue ----
   if constexpr (!kFused) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int mloc = wm * 64 + 16 * j + l16;
+    for (int j = 0; j < kTM; ++j) {
+      const int mloc = wm * kWM + 16 * j + l16;
       if (j < n_active && mloc < rows_valid) {
         const int64_t m = row0 + mloc;
 #pragma unroll
@@ -320,9 +328,12 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
     }
   } else {
     // h = silu(g) * u into the gate accumulators; per-token amax over this
-    // wave's 32 h columns, then across the 4 row-waves through LDS
+    // wave's 32 h columns, then across the 4 row-waves through LDS (aliased
+    // onto ring0 once every wave's loads have landed and reads are done)
+    float(*sAmax)[kBM] = reinterpret_cast<float(*)[kBM]>(ring0);
+    __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+    for (int j = 0; j < kTM; ++j) {
       float amax = 0.f;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
@@ -334,13 +345,13 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
         }
       amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
       amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-      if (q == 0) sAmax[wn][wm * 64 + 16 * j + l16] = amax;
+      if (q == 0) sAmax[wn][wm * kWM + 16 * j + l16] = amax;
     }
     __syncthreads();
     uint8_t* hq = reinterpret_cast<uint8_t*>(out);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int mloc = wm * 64 + 16 * j + l16;
+    for (int j = 0; j < kTM; ++j) {
+      const int mloc = wm * kWM + 16 * j + l16;
       if (j < n_active && mloc < rows_valid) {
         const float amax = fmaxf(fmaxf(sAmax[0][mloc], sAmax[1][mloc]), fmaxf(sAmax[2][mloc], sAmax[3][mloc]));
         const float sc = scale_from_amax(amax);
