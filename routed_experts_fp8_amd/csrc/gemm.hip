@@ -52,6 +52,8 @@
 #include "device_common.h"
 #include "host_common.h"
 
+#include <type_traits>
+
 namespace moefp8 {
 namespace {
 
@@ -74,6 +76,9 @@ constexpr int kOffS = kOffB + kBN * 128;         // [256] float: 192 activation 
 constexpr int kSB = 192;                         // float index of the weight-block scales in S
 constexpr int kStageBytes = kOffS + 4 * 64 * 4;  // 54272; 3 stages = 162816 B of LDS
 constexpr int kDmaPerChunk = 7;                  // per wave, see the memory pipeline notes
+constexpr int kMaxTilesPerWG = 64;              // tile-list entries per workgroup
+constexpr int kMaxNTiles = 2048;                 // n_tile field width of a tile-list entry
+constexpr int kPersistentMaxKB = 32;             // persistent launch for K <= 4096
 
 // LDS byte address of a __shared__ location.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -81,20 +86,29 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 }
 
 // Direct global -> LDS loads (gfx950 global_load_lds_dword[x4]): lane i's
-// 16 (4) bytes land at LDS address `lds` + 16 i (4 i).  Issued from inline
+// 16 (4) bytes, read from sbase + voff_i (scalar base, per-lane 32-bit
+// offset), land at LDS address `lds` + 16 i (4 i).  Issued from inline
 // assembly so that the compiler's wait-count pass does not track them: its
 // alias tracking of LDS DMA is coarse and would otherwise force every LDS
 // read in the K loop to wait for ALL outstanding DMA, serialising the ring.
-// The kernel waits for these loads itself (s_waitcnt vmcnt + s_barrier), and
-// no compiler-visible vector loads are in flight while they are.  The
-// instructions have no destination registers; the address VGPRs are read at
-// issue.
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" : : "s"(lds), "v"(g) : "memory", "m0");
+// The kernel waits for these loads itself (s_waitcnt vmcnt + s_barrier): no
+// compiler-visible vector loads are in flight while they are, and the
+// epilogue's stores can only delay a wait, never satisfy it early (loads
+// complete in issue order, and every store adds to the count).  The
+// instructions have no destination registers; the address VGPRs are read
+// at issue.
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" : : "s"(lds), "v"(voff), "s"(sbase)
+               : "memory", "m0");
 }
-__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" : : "s"(lds), "v"(g) : "memory", "m0");
+__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" : : "s"(lds), "v"(voff), "s"(sbase)
+               : "memory", "m0");
 }
+
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
+// accesses, not for its vector-memory loads (the ring's DMA stays in flight).
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 __device__ __forceinline__ v4f mfma_chunk(const v8i& a, const v8i& b) {
   const v4f zero = {0.f, 0.f, 0.f, 0.f};
@@ -105,10 +119,14 @@ __device__ __forceinline__ v4f mfma_chunk(const v8i& a, const v8i& b) {
 // Byte offset of logical 16-byte piece c16 of row r inside a [rows][128 B] tile.
 __device__ __forceinline__ int swz(int r, int c16) { return r * 128 + ((c16 ^ (r & 7)) << 4); }
 
-// 32 bytes of row r starting at logical byte 32 * q (q = lane / 16) -> v8i.
-__device__ __forceinline__ v8i lds_operand(const uint8_t* tile, int r, int q) {
-  const u32x4 lo = *reinterpret_cast<const u32x4*>(tile + swz(r, 2 * q));
-  const u32x4 hi = *reinterpret_cast<const u32x4*>(tile + swz(r, 2 * q + 1));
+// Operand rows are always 16 r0 + lane % 16, so row & 7 == lane & 7 and the
+// swizzled byte offsets of the lane's two 16-byte pieces (logical pieces 2q
+// and 2q + 1 of its row, q = lane / 16) are the same for every row:
+// lane_lo = 128 (lane % 16) + 16 (2q ^ (lane & 7)), lane_hi = lane_lo ^ 16.
+// The row block then enters as an immediate offset.
+__device__ __forceinline__ v8i lds_operand(const uint8_t* rows16, uint32_t lane_lo, uint32_t lane_hi) {
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(rows16 + lane_lo);
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(rows16 + lane_hi);
   v8i v;
   v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
   v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
@@ -119,25 +137,26 @@ template <int MODE>
 __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
     const uint8_t* __restrict__ aq, const float* __restrict__ as, const uint8_t* __restrict__ bq,
     const float* __restrict__ bs, const int* __restrict__ offsets, int G, int N, int K, int n_tiles,
-    void* __restrict__ out, float* __restrict__ hs_out) {
+    int wg_per_xcd, void* __restrict__ out, float* __restrict__ hs_out) {
   constexpr bool kFused = MODE == OUT_SWIGLU;
-  // three ring stages as separate LDS objects: the compiler can then tell a
-  // DMA into one stage from reads of another and adds no extra waits
-  __shared__ __attribute__((aligned(1024))) uint8_t ring0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring1[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) uint8_t ring2[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages * kStageBytes];
+  __shared__ int2 sTile[kMaxTilesPerWG];  // {g | n_tile << 10 | rows_valid << 21, row0}
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform (scalar) wave index
   const int wn = w & 3, wm = w >> 2;
   const int q = lane >> 4, l16 = lane & 15;
+  const int KB = K / 128;
+  const int I = N / 2;  // fused: gate rows [0, I), up rows [I, 2I)
+  const int nblk = N / 128;
 
-  // ---- tile table (LDS scratch aliased onto the ring) ----
-  int* sP = reinterpret_cast<int*>(ring0);                // [G + 1]
-  int* sOff = sP + (kMaxGroups + 1);                      // [G + 1]
-  int* sScan = sOff + (kMaxGroups + 1);                   // [kThreads]
+  // ---- this workgroup's tile list (group table scratch aliased onto the ring) ----
+  int n_my;
   {
+    int* sP = reinterpret_cast<int*>(ring);  // [G + 1] m-tile prefix
+    int* sOff = sP + (kMaxGroups + 1);       // [G + 1] row offsets
+    int* sScan = sOff + (kMaxGroups + 1);    // [kThreads]
     int mt[2];
     int local = 0;
 #pragma unroll
@@ -169,119 +188,153 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
     }
     if (tid == kThreads - 1) sP[G] = sScan[kThreads - 1];
     __syncthreads();
-  }
-  const int total = sP[G] * n_tiles;
-  const int per_xcd = (total + 7) / 8;
-  const int slot = blockIdx.x >> 3;
-  if (slot >= per_xcd) return;
-  const int lid = (blockIdx.x & 7) * per_xcd + slot;
-  if (lid >= total) return;
-  int g;
-  {
-    int lo = 0, hi = G;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (sP[mid] * n_tiles <= lid) lo = mid; else hi = mid - 1;
+    // XCD x sweeps logical tiles [x * per_xcd, (x + 1) * per_xcd); its
+    // workgroup s takes every wg_per_xcd-th of them, starting at s
+    const int total = sP[G] * n_tiles;
+    const int per_xcd = (total + 7) / 8;
+    const int lo = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+    const int hi = min(total, (int)(blockIdx.x & 7) * per_xcd + per_xcd);
+    n_my = lo < hi ? min((hi - lo + wg_per_xcd - 1) / wg_per_xcd, kMaxTilesPerWG) : 0;
+    if (tid < n_my) {
+      const int lid = lo + tid * wg_per_xcd;
+      int lo_g = 0, hi_g = G;
+      while (lo_g < hi_g) {
+        const int mid = (lo_g + hi_g + 1) >> 1;
+        if (sP[mid] * n_tiles <= lid) lo_g = mid; else hi_g = mid - 1;
+      }
+      const int g = lo_g;
+      const int mt_g = sP[g + 1] - sP[g];
+      const int local_id = lid - sP[g] * n_tiles;
+      const int n_tile = local_id / mt_g;
+      const int row0 = sOff[g] + (local_id % mt_g) * kBM;
+      const int rows_valid = min(kBM, sOff[g + 1] - row0);
+      sTile[tid] = make_int2(g | (n_tile << 10) | (rows_valid << 21), row0);
     }
-    g = lo;
+    __syncthreads();  // tile list visible; the ring is free again
   }
-  const int mt_g = sP[g + 1] - sP[g];
-  const int local_id = lid - sP[g] * n_tiles;
-  const int n_tile = local_id / mt_g;
-  const int m_tile = local_id % mt_g;
-  const int row0 = sOff[g] + m_tile * kBM;
-  const int rows_valid = min(kBM, sOff[g + 1] - row0);
-  const int KB = K / 128;
-  const int I = N / 2;  // fused: gate rows [0, I), up rows [I, 2I)
-  const uint8_t* bq_g = bq + (int64_t)g * N * K;
-  const float* bs_g = bs + (int64_t)g * (N / 128) * KB;
-  // the two 128-row weight blocks of this tile
-  const int nblk = N / 128;
-  const int blkA = kFused ? n_tile : 2 * n_tile;
-  const int blkB = kFused ? I / 128 + n_tile : min(2 * n_tile + 1, nblk - 1);
+  if (n_my == 0) return;
 
-  // ---- per-lane global row pointers of this wave's DMA slices ----
-  const int p16 = lane & 7;           // physical 16-byte piece inside the LDS row
-  const int rsub = lane >> 3;         // row inside the 8-row (1 KB) DMA slice
-  const int c16 = p16 ^ rsub;         // logical piece it must fetch (swizzle)
-  // activation slices (8 rows each): waves 0-3 take 3, waves 4-7 take 2
+  // ---- issue side: one continuous chunk stream over all of this workgroup's tiles ----
+  const int p16 = lane & 7;   // physical 16-byte piece inside the LDS row
+  const int rsub = lane >> 3;  // row inside the 8-row (1 KB) DMA slice
+  const int c16 = p16 ^ rsub;  // logical piece it must fetch (swizzle)
+  // activation slices (8 rows each): waves 0-3 take 3, waves 4-7 take 2; the
+  // scale load of waves 4-7 fills S: S[t] = sa of token t (t < 192, rows
+  // past the group clamped), S[192] / S[193] = weight-block scales A / B
   const bool a3 = w < 4;
   const int a_slice0 = a3 ? 3 * w : 12 + 2 * (w - 4);
-  const uint8_t* a_src[3];
+  const uint8_t* ia_base = aq;  // scalar bases of the tile being issued
+  const uint8_t* ib_base = bq;
+  const uint8_t* is_base = reinterpret_cast<const uint8_t*>(as);
+  uint32_t ia_off[3], ib_off[4], is_off = 0;  // per-lane byte offsets from them
+  int it = 0, ikb = 0;                         // next chunk to issue: tile it, chunk ikb
+  auto load_issue_tile = [&](int i) {
+    const int2 e = sTile[i];
+    const int wd = __builtin_amdgcn_readfirstlane(e.x);
+    const int row0 = __builtin_amdgcn_readfirstlane(e.y);
+    const int g = wd & 1023, n_tile = (wd >> 10) & 2047, rows_valid = wd >> 21;
+    ia_base = aq + (int64_t)row0 * K;
 #pragma unroll
-  for (int i = 0; i < 3; ++i) {
-    const int r = (a_slice0 + i) * 8 + rsub;
-    a_src[i] = aq + (int64_t)(row0 + min(r, rows_valid - 1)) * K + c16 * 16;
-  }
-  const uint8_t* b_src[4];
+    for (int j = 0; j < 3; ++j)
+      ia_off[j] = (uint32_t)(min((a_slice0 + j) * 8 + rsub, rows_valid - 1) * K + c16 * 16);
+    const uint8_t* bq_g = bq + (int64_t)g * N * K;
+    if (kFused) {
+      // waves 0-3 fetch gate block n_tile, waves 4-7 the matching up block
+      ib_base = bq_g + (int64_t)((w < 4 ? 0 : I) + n_tile * 128) * K;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = (w * 4 + i) * 8 + rsub;
-    int wrow;
-    if (kFused) wrow = r < 128 ? n_tile * 128 + r : I + n_tile * 128 + (r - 128);
-    else wrow = min(n_tile * kBN + r, N - 1);
-    b_src[i] = bq_g + (int64_t)wrow * K + c16 * 16;
-  }
-  // scale loads (waves 4-7): S[t] = sa of token t for t < 192 (rows past the
-  // group clamped), S[192] / S[193] = the scales of weight blocks A / B
-  const float* s_src = as;
-  if (w >= 4 && w < 7) s_src = as + (int64_t)(row0 + min((w - 4) * 64 + lane, rows_valid - 1)) * KB;
-  else s_src = bs_g + (int64_t)(lane == 0 ? blkA : blkB) * KB;
-  __syncthreads();  // tile-table scratch (aliased onto ring0) is about to be overwritten
-
-  auto issue = [&](int kb, uint8_t* st) {
-    const uint32_t base = __builtin_amdgcn_readfirstlane(lds_addr(st));
+      for (int j = 0; j < 4; ++j) ib_off[j] = (uint32_t)((((w & 3) * 4 + j) * 8 + rsub) * K + c16 * 16);
+    } else {
+      ib_base = bq_g + (int64_t)n_tile * kBN * K;
+      const int last = N - 1 - n_tile * kBN;  // rows past N (a half tile) re-read row N - 1
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma16(a_src[i] + kb * 128, base + kOffA + (a_slice0 + i) * 1024);
-    if (a3) dma16(a_src[2] + kb * 128, base + kOffA + (a_slice0 + 2) * 1024);
-    else dma4(s_src + kb, base + kOffS + (w - 4) * 256);
+      for (int j = 0; j < 4; ++j) ib_off[j] = (uint32_t)(min((w * 4 + j) * 8 + rsub, last) * K + c16 * 16);
+    }
+    if (w < 7) {
+      is_base = reinterpret_cast<const uint8_t*>(as + (int64_t)row0 * KB);
+      is_off = (uint32_t)(min((w - 4) * 64 + lane, rows_valid - 1) * KB * 4);
+    } else {
+      const int blkA = kFused ? n_tile : 2 * n_tile;
+      const int blkB = kFused ? I / 128 + n_tile : min(2 * n_tile + 1, nblk - 1);
+      is_base = reinterpret_cast<const uint8_t*>(bs + ((int64_t)g * nblk + blkA) * KB);
+      is_off = (uint32_t)(lane == 0 ? 0 : (blkB - blkA) * KB * 4);
+    }
+  };
+  // Enqueue chunk (it, ikb) into the stage at LDS address `st`, then advance;
+  // past the last chunk the last chunk is re-fetched, so every call issues
+  // exactly kDmaPerChunk loads per wave.
+  auto issue_next = [&](uint32_t st) {
+    const uint8_t* a = ia_base + ikb * 128;
+    const uint8_t* b = ib_base + ikb * 128;
+    dma16(a, ia_off[0], st + kOffA + a_slice0 * 1024);
+    dma16(a, ia_off[1], st + kOffA + (a_slice0 + 1) * 1024);
+    if (a3) dma16(a, ia_off[2], st + kOffA + (a_slice0 + 2) * 1024);
+    else dma4(is_base + ikb * 4, is_off, st + kOffS + (w - 4) * 256);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma16(b_src[i] + kb * 128, base + kOffB + (w * 4 + i) * 1024);
+    for (int j = 0; j < 4; ++j) dma16(b, ib_off[j], st + kOffB + (w * 4 + j) * 1024);
+    if (ikb + 1 < KB) {
+      ++ikb;
+    } else if (it + 1 < n_my) {
+      ++it;
+      ikb = 0;
+      load_issue_tile(it);
+    }
   };
 
   // ---- wave geometry ----
-  int brow[4];  // row of n-tile i inside the weight tile, for this lane
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    brow[i] = kFused ? (i < 2 ? 0 : 128) + 32 * wn + 16 * (i & 1) + l16 : 64 * wn + 16 * i + l16;
-  int n_active = 0;
-#pragma unroll
-  for (int j = 0; j < kTM; ++j)
-    if (wm * kWM + 16 * j < rows_valid) n_active = j + 1;
-  const bool wave_rows_valid = kFused || (n_tile * kBN + wn * 64 < N);
-  if (!wave_rows_valid) n_active = 0;
+  const uint32_t lane_lo = l16 * 128 + (((2 * q) ^ (l16 & 7)) << 4);
+  const uint32_t lane_hi = lane_lo ^ 16;
+  // first weight row of instruction tile i (rows 16 i' + lane % 16)
+  auto brow0 = [&](int i) { return kFused ? (i < 2 ? 0 : 128) + 32 * wn + 16 * (i & 1) : 64 * wn + 16 * i; };
   const int sb_sel = kFused ? 0 : (wn >> 1);  // unfused: rows of waves 0,1 in block A, 2,3 in B
 
-  v4f acc[4][kTM];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < kTM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(ring));
+  load_issue_tile(0);
+  issue_next(ring_lds);
+  issue_next(ring_lds + kStageBytes);
+  int ist = 2, cst = 0;  // stage receiving the next issue / holding the next chunk to multiply
 
-  // Every step issues exactly kDmaPerChunk loads, so "chunk kb has landed" is
-  // always vmcnt(kDmaPerChunk): past the end the last chunk is re-fetched (an
-  // L2 hit) into the free stage instead of issuing nothing.
-  issue(0, ring0);
-  issue(min(1, KB - 1), ring1);
+  for (int ti = 0; ti < n_my; ++ti) {
+    const int2 e = sTile[ti];
+    const int wd = __builtin_amdgcn_readfirstlane(e.x);
+    const int row0 = __builtin_amdgcn_readfirstlane(e.y);
+    const int n_tile = (wd >> 10) & 2047, rows_valid = wd >> 21;
+    int n_active = 0;
+#pragma unroll
+    for (int j = 0; j < kTM; ++j)
+      if (wm * kWM + 16 * j < rows_valid) n_active = j + 1;
+    if (!kFused && n_tile * kBN + wn * 64 >= N) n_active = 0;  // half tile: rows past N
 
-  // One K step on the stage holding chunk kb; `nxt` receives chunk kb + 2.
-  auto step = [&](int kb, const uint8_t* st, uint8_t* nxt) {
-    // this wave's loads of chunk kb have landed (only chunk kb+1's may still fly) ...
-    __builtin_amdgcn_s_waitcnt(0x0F70 | kDmaPerChunk);
-    // ... and every other wave's too; all waves are also done with chunk kb-1,
-    // whose stage `nxt` is refilled now
-    __builtin_amdgcn_s_barrier();
-    issue(min(kb + 2, KB - 1), nxt);
-    const float* sS = reinterpret_cast<const float*>(st + kOffS);
-    v8i a_op[4];
+    v4f acc[4][kTM];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a_op[i] = lds_operand(st + kOffB, brow[i], q);
-    const float sb0 = kFused ? sS[kSB] : sS[kSB + sb_sel];
-    const float sb1 = kFused ? sS[kSB + 1] : sb0;
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < kTM; ++j) {
-      if (j < n_active) {
-        const v8i b_op = lds_operand(st + kOffA, wm * kWM + 16 * j + l16, q);
+      for (int j = 0; j < kTM; ++j) acc[i][j] = v4f{0.f, 0.f, 0.f, 0.f};
+
+    const uint8_t* st = ring;
+    for (int kb = 0; kb < KB; ++kb) {
+      // this wave's loads of the chunk in stage cst have landed (only the next
+      // chunk's may still fly; loads complete in issue order) ...
+      __builtin_amdgcn_s_waitcnt(0x0F70 | kDmaPerChunk);
+      // ... and every other wave's too; all waves are also done with the
+      // previous chunk, whose stage receives the chunk after next now
+      __builtin_amdgcn_s_barrier();
+      issue_next(ring_lds + ist * kStageBytes);
+      ist = ist == kStages - 1 ? 0 : ist + 1;
+      st = ring + cst * kStageBytes;
+      cst = cst == kStages - 1 ? 0 : cst + 1;
+
+      const float* sS = reinterpret_cast<const float*>(st + kOffS);
+      v8i a_op[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a_op[i] = lds_operand(st + kOffB + brow0(i) * 128, lane_lo, lane_hi);
+      const float sb0 = kFused ? sS[kSB] : sS[kSB + sb_sel];
+      const float sb1 = kFused ? sS[kSB + 1] : sb0;
+      // active tiles are a prefix (j < n_active): leaving at the first
+      // inactive one gives the compiler one nested region to schedule
+#pragma unroll
+      for (int j = 0; j < kTM; ++j) {
+        if (j >= n_active) break;
+        const v8i b_op = lds_operand(st + kOffA + (wm * kWM + 16 * j) * 128, lane_lo, lane_hi);
         const float sa = sS[wm * kWM + 16 * j + l16];
         const float sc0 = sa * sb0;
         const float sc1 = kFused ? sa * sb1 : sc0;
@@ -296,77 +349,87 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
         }
       }
     }
-  };
-  for (int kb = 0; kb < KB; kb += 3) {
-    step(kb, ring0, ring2);
-    if (kb + 1 < KB) step(kb + 1, ring1, ring0);
-    if (kb + 2 < KB) step(kb + 2, ring2, ring1);
-  }
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // drain the trailing re-fetches
 
-  // ---- epilogue ----
-  if constexpr (!kFused) {
+    // ---- epilogue (the next tile's first chunks keep streaming in) ----
+    if constexpr (!kFused) {
 #pragma unroll
-    for (int j = 0; j < kTM; ++j) {
-      const int mloc = wm * kWM + 16 * j + l16;
-      if (j < n_active && mloc < rows_valid) {
-        const int64_t m = row0 + mloc;
+      for (int j = 0; j < kTM; ++j) {
+        const int mloc = wm * kWM + 16 * j + l16;
+        if (j < n_active && mloc < rows_valid) {
+          const int64_t m = row0 + mloc;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = n_tile * kBN + wn * 64 + 16 * i + 4 * q;
-          if (MODE == OUT_F32) {
-            float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
-            *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + m * N + n) = v;
-          } else {
-            uint2 v;
-            v.x = bf16_rne_bits(acc[i][j][0]) | (bf16_rne_bits(acc[i][j][1]) << 16);
-            v.y = bf16_rne_bits(acc[i][j][2]) | (bf16_rne_bits(acc[i][j][3]) << 16);
-            *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + m * N + n) = v;
+          for (int i = 0; i < 4; ++i) {
+            const int n = n_tile * kBN + wn * 64 + 16 * i + 4 * q;
+            if (MODE == OUT_F32) {
+              float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+              *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + m * N + n) = v;
+            } else {
+              uint2 v;
+              v.x = bf16_rne_bits(acc[i][j][0]) | (bf16_rne_bits(acc[i][j][1]) << 16);
+              v.y = bf16_rne_bits(acc[i][j][2]) | (bf16_rne_bits(acc[i][j][3]) << 16);
+              *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(out) + m * N + n) = v;
+            }
           }
         }
       }
-    }
-  } else {
-    // h = silu(g) * u into the gate accumulators; per-token amax over this
-    // wave's 32 h columns, then across the 4 row-waves through LDS (aliased
-    // onto ring0 once every wave's loads have landed and reads are done)
-    float(*sAmax)[kBM] = reinterpret_cast<float(*)[kBM]>(ring0);
-    __syncthreads();
+    } else {
+      // h = silu(g) * u into the gate accumulators; per-token amax over this
+      // wave's 32 h columns, then across the 4 row-waves through LDS.  The
+      // exchange uses the stage just multiplied: it is not refilled before
+      // the next K step's barrier.
+      float(*sAmax)[kBM] = reinterpret_cast<float(*)[kBM]>(const_cast<uint8_t*>(st));
+      lds_barrier();  // every wave is done reading that stage
 #pragma unroll
-    for (int j = 0; j < kTM; ++j) {
-      float amax = 0.f;
+      for (int j = 0; j < kTM; ++j) {
+        float amax = 0.f;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float h = spec_silu(acc[i][j][v]) * acc[i + 2][j][v];
-          acc[i][j][v] = h;
-          amax = fmaxf(amax, fabsf(h));
+          for (int v = 0; v < 4; ++v) {
+            const float h = spec_silu(acc[i][j][v]) * acc[i + 2][j][v];
+            acc[i][j][v] = h;
+            amax = fmaxf(amax, fabsf(h));
+          }
+        amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+        if (q == 0) sAmax[wn][wm * kWM + 16 * j + l16] = amax;
+      }
+      lds_barrier();  // partial maxima visible
+      uint8_t* hq = reinterpret_cast<uint8_t*>(out);
+#pragma unroll
+      for (int j = 0; j < kTM; ++j) {
+        const int mloc = wm * kWM + 16 * j + l16;
+        if (j < n_active && mloc < rows_valid) {
+          const float amax = fmaxf(fmaxf(sAmax[0][mloc], sAmax[1][mloc]), fmaxf(sAmax[2][mloc], sAmax[3][mloc]));
+          const float sc = scale_from_amax(amax);
+          const int64_t m = row0 + mloc;
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const int col = n_tile * 128 + 32 * wn + 16 * i + 4 * q;
+            const uint32_t wd4 = quantize(acc[i][j][0], sc) | (quantize(acc[i][j][1], sc) << 8) |
+                                 (quantize(acc[i][j][2], sc) << 16) | (quantize(acc[i][j][3], sc) << 24);
+            *reinterpret_cast<uint32_t*>(hq + m * I + col) = wd4;
+          }
+          if (wn == 0 && q == 0) hs_out[m * (I / 128) + n_tile] = sc;
         }
-      amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
-      amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
-      if (q == 0) sAmax[wn][wm * kWM + 16 * j + l16] = amax;
-    }
-    __syncthreads();
-    uint8_t* hq = reinterpret_cast<uint8_t*>(out);
-#pragma unroll
-    for (int j = 0; j < kTM; ++j) {
-      const int mloc = wm * kWM + 16 * j + l16;
-      if (j < n_active && mloc < rows_valid) {
-        const float amax = fmaxf(fmaxf(sAmax[0][mloc], sAmax[1][mloc]), fmaxf(sAmax[2][mloc], sAmax[3][mloc]));
-        const float sc = scale_from_amax(amax);
-        const int64_t m = row0 + mloc;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int col = n_tile * 128 + 32 * wn + 16 * i + 4 * q;
-          const uint32_t wd = quantize(acc[i][j][0], sc) | (quantize(acc[i][j][1], sc) << 8) |
-                              (quantize(acc[i][j][2], sc) << 16) | (quantize(acc[i][j][3], sc) << 24);
-          *reinterpret_cast<uint32_t*>(hq + m * I + col) = wd;
-        }
-        if (wn == 0 && q == 0) hs_out[m * (I / 128) + n_tile] = sc;
       }
     }
   }
+  // the trailing re-fetches must land before the workgroup's LDS is released
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
+
+// Compute units of the current device (cached per device).
+int device_cu_count() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
 }
 
 template <int MODE>
@@ -374,14 +437,29 @@ moe_status launch_gemm(const uint8_t* aq, const float* as, const uint8_t* bq, co
                        const int* offsets, int G, int64_t M, int N, int K, void* out, float* hs,
                        hipStream_t st, const char* what) {
   const int n_tiles = MODE == OUT_SWIGLU ? (N / 2) / 128 : (N + kBN - 1) / kBN;
+  if (n_tiles > kMaxNTiles) return fail(MOE_ERR_UNSUPPORTED, "%s: N=%d too large", what, N);
+  // Upper bound on the m-tiles: sum_g ceil(M_g / BM) <= floor(M / BM) + G, and
+  // every m-tile holds at least one row.
   int64_t mt_bound = M / kBM + G;
   if (mt_bound > M) mt_bound = M;
   const int64_t tiles = mt_bound * n_tiles;
-  const int64_t grid = (tiles + 7) / 8 * 8;
-  if (grid >= (1LL << 31)) return fail(MOE_ERR_UNSUPPORTED, "%s: too many tiles", what);
-  if (grid == 0) return MOE_OK;
-  grouped_gemm_kernel<MODE><<<(unsigned)grid, kThreads, 0, st>>>(aq, as, bq, bs, offsets, G, N, K, n_tiles,
-                                                                 out, hs);
+  if (tiles == 0) return MOE_OK;
+  if (tiles >= (1LL << 31)) return fail(MOE_ERR_UNSUPPORTED, "%s: too many tiles", what);
+  // Short tiles (K <= 128 kPersistentMaxKB): one resident workgroup per
+  // compute unit (the LDS ring fills a CU) walks a list of tiles with the
+  // ring running across tile boundaries, which hides the per-tile pipeline
+  // fill, table build and epilogue; at most kMaxTilesPerWG tiles each.  Long
+  // tiles: one tile per workgroup, so the dispatcher balances the tail.
+  const int64_t per_xcd = (tiles + 7) / 8;
+  int64_t wg_per_xcd = per_xcd;
+  if (K / 128 <= kPersistentMaxKB) {
+    wg_per_xcd = (device_cu_count() + 7) / 8;
+    const int64_t need = (per_xcd + kMaxTilesPerWG - 1) / kMaxTilesPerWG;
+    if (wg_per_xcd < need) wg_per_xcd = need;
+    if (wg_per_xcd > per_xcd) wg_per_xcd = per_xcd;
+  }
+  grouped_gemm_kernel<MODE><<<(unsigned)(8 * wg_per_xcd), kThreads, 0, st>>>(
+      aq, as, bq, bs, offsets, G, N, K, n_tiles, (int)wg_per_xcd, out, hs);
   return after_launch(what, st);
 }
 

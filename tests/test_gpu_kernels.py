@@ -241,6 +241,33 @@ def test_grouped_gemm_bf16_is_rounded_f32(sizes, N, K):
     assert np.array_equal(bf16_bits(c16), bf16_bits(c32.to(torch.bfloat16)))
 
 
+def _random_codes(rng, shape):
+    """E4M3 codes of magnitude 2^-3 .. 2^4 with random signs (no NaN)."""
+    return (rng.integers(0x20, 0x58, shape) | (rng.integers(0, 2, shape) << 7)).astype(np.uint8)
+
+
+@pytest.mark.parametrize("K", [128, 384])
+def test_grouped_gemm_many_tiles_short_k(K):
+    """800 tiles with K of one or three 128-chunks: each workgroup runs
+    several tiles back to back, its load stream crossing tile boundaries
+    (up to two tiles ahead at K = 128), with ragged one-row m-tiles.
+    Operands are random codes and scales (the GEMM's contract)."""
+    sizes = [161, 1, 40, 100] * 40
+    G, M, N = len(sizes), sum(sizes), 1024
+    aq, bq = _random_codes(RNG, (M, K)), _random_codes(RNG, (G, N, K))
+    as_ = RNG.uniform(0.5, 2.0, (M, K // 128)).astype(np.float32)
+    bs = RNG.uniform(0.5, 2.0, (G, N // 128, K // 128)).astype(np.float32)
+    off = rand_offsets(RNG, sizes)
+    args = [to_dev(v) for v in (aq, as_, bq, bs, off)]
+    c = R.grouped_gemm_fp8_blockscaled(*args)
+    C, Mag = O.grouped_gemm(aq, as_, bq, bs, off)
+    assert_gemm_close(np_(c), C, Mag)
+    # fused SwiGLU over the same tile stream (I = 512: 4 tiles per m-tile)
+    hq, hs = R.grouped_gemm_fp8_swiglu(*args)
+    hq2, hs2 = R.swiglu(c)
+    assert np.array_equal(np_(hq), np_(hq2)) and np.array_equal(np_(hs), np_(hs2))
+
+
 def test_grouped_gemm_exact_integers():
     """Integer codes with unit scales: every partial sum is an integer below
     2^24, so the float32 result must equal the exact integer product."""
