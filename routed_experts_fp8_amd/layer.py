@@ -35,7 +35,7 @@ class MoEForward:
     """Preallocated buffers for one layer shape; ``__call__`` enqueues the
     whole forward on the current stream and returns y (bf16 [T, H])."""
 
-    def __init__(self, T, H, E, I, route, weights, device, fused=True, shared_I=None):
+    def __init__(self, T, H, E, I, route, weights, device, fused=True, shared_I=None, overlap_shared=True):
         self.T, self.H, self.E, self.I = T, H, E, I
         self.route = dict(route)
         self.K = route["K"] if route["mode"] == "sigmoid_bias" else route["n_groups"] * route["k_per_group"]
@@ -58,6 +58,11 @@ class MoEForward:
         )
         if not fused:
             self.buf["c1"] = e((M, 2 * I), torch.float32)
+        # The shared expert only needs x's FP8 codes, so it can run on a side
+        # stream beside the permutation and the routed GEMMs: its GEMMs are
+        # dense and compute-heavy while the routed ones stream weights from
+        # HBM, and the two fill each other's idle units.
+        self.side = torch.cuda.Stream(device=dev) if (shared_I and overlap_shared) else None
         if shared_I:
             self.buf.update(shq=e((T, shared_I), torch.uint8), shs=e((T, shared_I // 128), torch.float32),
                             sc2=e((T, H), torch.float32))
@@ -76,7 +81,9 @@ class MoEForward:
 
     def __call__(self, x, logits, bias=None, on_stage=None):
         """Enqueue the forward.  on_stage(name), if given, is called after each
-        stage is enqueued (the bench records a HIP event there)."""
+        stage is enqueued on the caller's stream (the bench records a HIP event
+        there).  With the shared expert on the side stream its GEMMs are not
+        marked; "shared_join" marks the caller's stream waiting for them."""
         mark = on_stage or (lambda name: None)
         b, w, r = self.buf, self.w, self.route
         if r["mode"] == "sigmoid_bias":
@@ -88,17 +95,29 @@ class MoEForward:
         mark("route")
         L.quant_act_1x128_e4m3(x, q=b["xq"], scale=b["xs"])
         mark("quant_act")
+        shared = None
+        if self.shared_I and self.side is not None:
+            # forked as soon as x's codes exist: the permutation and the routed
+            # GEMM1 then fill the CUs the shared GEMMs' last partial wave of
+            # workgroups leaves idle
+            self.side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(self.side):
+                self._ffn(b["xq"], b["xs"], b["one_group"], w["sw13q"], w["sw13s"], w["sw2q"], w["sw2s"],
+                          b["shq"], b["shs"], b["sc2"], b.get("sc1"), lambda n: None)
+            shared = b["sc2"]
         L.moe_permute(b["idx"], self.E, b["xq"], b["xs"], workspace=b["ws"],
                       out=dict(offsets=b["offsets"], dst_row=b["dst_row"], src_token=b["src_token"],
                                aq=b["aq"], **{"as": b["as_"]}))
         mark("permute")
         self._ffn(b["aq"], b["as_"], b["offsets"], w["w13q"], w["w13s"], w["w2q"], w["w2s"],
                   b["hq"], b["hs"], b["c2"], b.get("c1"), mark)
-        shared = None
-        if self.shared_I:
+        if self.shared_I and self.side is None:
             self._ffn(b["xq"], b["xs"], b["one_group"], w["sw13q"], w["sw13s"], w["sw2q"], w["sw2s"],
                       b["shq"], b["shs"], b["sc2"], b.get("sc1"), lambda n: mark("shared_" + n))
             shared = b["sc2"]
+        elif self.side is not None:
+            torch.cuda.current_stream().wait_stream(self.side)
+            mark("shared_join")
         L.moe_combine(b["c2"], b["dst_row"], b["gate"], shared, out=b["y"])
         mark("combine")
         return b["y"]

@@ -38,11 +38,11 @@ def _variant(name):
     return cfg
 
 
-def run_layer(cfg, fused, seed=0):
+def run_layer(cfg, fused, seed=0, overlap_shared=True):
     d = synth.layer_inputs(cfg, dev(), seed=seed)
     w = R.quantize_weights(d["w13"], d["w2"], d.get("sw13"), d.get("sw2"))
     fwd = R.MoEForward(cfg["T"], cfg["H"], cfg["E"], cfg["I"], cfg["route"], w, dev(), fused=fused,
-                       shared_I=cfg.get("shared_I"))
+                       shared_I=cfg.get("shared_I"), overlap_shared=overlap_shared)
     y = fwd(d["x"], d["logits"], d["bias"])
     torch.cuda.synchronize()
     return d, w, fwd, y
@@ -139,3 +139,17 @@ def test_layer_fused_equals_unfused_and_is_deterministic():
     _, _, _, y3 = run_layer(cfg, True)
     assert np.array_equal(bf16_bits(y1), bf16_bits(y2))
     assert np.array_equal(bf16_bits(y1), bf16_bits(y3))
+
+
+def test_layer_shared_expert_side_stream_equals_in_line():
+    """The shared expert on its own stream (the default) and in line on the
+    caller's stream give the same bits, over repeated calls of one layer
+    object (buffers reused across steps)."""
+    cfg = _variant("tiny_sigmoid_shared")
+    d, _, fwd, y1 = run_layer(cfg, True, overlap_shared=True)
+    _, _, _, y2 = run_layer(cfg, True, overlap_shared=False)
+    assert np.array_equal(bf16_bits(y1), bf16_bits(y2))
+    for _ in range(3):
+        y = fwd(d["x"], d["logits"], d["bias"])
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(y), bf16_bits(y2))
