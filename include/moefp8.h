@@ -183,19 +183,25 @@ MOE_API moe_status quant_weight_128x128_e4m3(const void* w, moe_dtype w_dtype, i
  * output per chunk), in chunk order.
  *
  *  aq  u8 [M, K], as f32 [M, K/128]           activations, 1x128 tiles
+ *  a_row  i32 [M] or NULL   optional row gather: row m of the grouped operand
+ *         is row a_row[m] of aq / as, which then have a_rows rows (the
+ *         permutation's src_token turns the token-order codes into the
+ *         expert-grouped operand without a permuted copy).  Indices outside
+ *         [0, a_rows) are clamped into it.  NULL: aq / as have M rows and
+ *         a_rows is ignored.  With a_row, a_rows * K must be <= 2^32.
  *  bq  u8 [G, N, K], bs f32 [G, N/128, K/128] weights ([out, in] per group)
  *  group_offsets i32 [G+1] (device)           offsets[G] == M
  *  c   f32 or bf16 [M, N] (out); bf16 output is the RNE rounding of the
  *      float32 result.  Rows of empty groups do not exist; every row of C is
  *      written.
  *  Sizes: M >= 0, 1 <= G <= 1024, N % 128 == 0, K % 128 == 0.
- * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED (G > 1024),
- *         MOE_ERR_ALIGN.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED (G > 1024, K >
+ *         65536, a gathered operand above 4 GiB), MOE_ERR_ALIGN.
  */
-MOE_API moe_status grouped_gemm_fp8_blockscaled(const uint8_t* aq, const float* as, const uint8_t* bq,
-                                        const float* bs, const int32_t* group_offsets, int32_t G,
-                                        int64_t M, int32_t N, int32_t K, void* c,
-                                        moe_dtype c_dtype, void* stream);
+MOE_API moe_status grouped_gemm_fp8_blockscaled(const uint8_t* aq, const float* as, const int32_t* a_row,
+                                        int64_t a_rows, const uint8_t* bq, const float* bs,
+                                        const int32_t* group_offsets, int32_t G, int64_t M, int32_t N,
+                                        int32_t K, void* c, moe_dtype c_dtype, void* stream);
 
 /*
  * grouped_gemm_fp8_swiglu -- the gate|up grouped GEMM with SwiGLU and 1x128
@@ -207,15 +213,16 @@ MOE_API moe_status grouped_gemm_fp8_blockscaled(const uint8_t* aq, const float* 
  * binary32 sigmoid specification of moe_route, and quantises h in 1x128 tiles
  * along I.  The float32 G1 is never written.
  *
+ *  aq, as, a_row, a_rows: as for grouped_gemm_fp8_blockscaled
  *  bq  u8 [G, 2I, K]: rows [0, I) are the gate projection, [I, 2I) the up
- *  hq  u8 [M, I], hs f32 [M, I/128]   (out)
+ *  hq  u8 [M, I], hs f32 [M, I/128]   (out, in grouped row order)
  *  Sizes: I % 128 == 0, K % 128 == 0.
  * Errors: as grouped_gemm_fp8_blockscaled.
  */
-MOE_API moe_status grouped_gemm_fp8_swiglu(const uint8_t* aq, const float* as, const uint8_t* bq,
-                                   const float* bs, const int32_t* group_offsets, int32_t G,
-                                   int64_t M, int32_t I, int32_t K, uint8_t* hq, float* hs,
-                                   void* stream);
+MOE_API moe_status grouped_gemm_fp8_swiglu(const uint8_t* aq, const float* as, const int32_t* a_row,
+                                   int64_t a_rows, const uint8_t* bq, const float* bs,
+                                   const int32_t* group_offsets, int32_t G, int64_t M, int32_t I,
+                                   int32_t K, uint8_t* hq, float* hs, void* stream);
 
 /*
  * swiglu -- standalone SwiGLU + 1x128 FP8 quantisation.           [DSV3-FP8]

@@ -30,10 +30,10 @@ _SIGNATURES = {
     "quant_act_1x128_e4m3": (_i32, [_c_void_p, _i32, _i64, _i32, _c_void_p, _c_void_p, _c_void_p]),
     "quant_weight_128x128_e4m3": (_i32, [_c_void_p, _i32, _i32, _i32, _i32, _c_void_p, _c_void_p,
                                          _c_void_p]),
-    "grouped_gemm_fp8_blockscaled": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p,
-                                            _i32, _i64, _i32, _i32, _c_void_p, _i32, _c_void_p]),
-    "grouped_gemm_fp8_swiglu": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32,
-                                       _i64, _i32, _i32, _c_void_p, _c_void_p, _c_void_p]),
+    "grouped_gemm_fp8_blockscaled": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p, _c_void_p,
+                                            _c_void_p, _i32, _i64, _i32, _i32, _c_void_p, _i32, _c_void_p]),
+    "grouped_gemm_fp8_swiglu": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p, _c_void_p,
+                                       _c_void_p, _i32, _i64, _i32, _i32, _c_void_p, _c_void_p, _c_void_p]),
     "swiglu": (_i32, [_c_void_p, _i64, _i32, _c_void_p, _c_void_p, _c_void_p]),
     "moe_combine": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _c_void_p,
                            _c_void_p]),
@@ -195,37 +195,44 @@ def quant_weight_128x128_e4m3(w, q=None, scale=None):
     return q, scale
 
 
-def _gemm_operands(aq, as_, bq, bs, offsets):
+def _gemm_operands(aq, as_, bq, bs, offsets, a_row):
     _need(aq, "aq", torch.uint8)
-    M, K = aq.shape
-    _need(as_, "as", torch.float32, (M, K // 128))
+    A, K = aq.shape
+    _need(as_, "as", torch.float32, (A, K // 128))
+    if a_row is not None:
+        _need(a_row, "a_row", torch.int32)
+        if a_row.dim() != 1:
+            raise ValueError("a_row must be 1-D [M]")
+    M = A if a_row is None else a_row.shape[0]
     _need(bq, "bq", torch.uint8)
     G, N, K2 = bq.shape
     if K2 != K:
         raise ValueError(f"bq reduction dim {K2} != aq's {K}")
     _need(bs, "bs", torch.float32, (G, N // 128, K // 128))
     _need(offsets, "group_offsets", torch.int32, (G + 1,))
-    return M, K, G, N
+    return M, K, G, N, A
 
 
-def grouped_gemm_fp8_blockscaled(aq, as_, bq, bs, offsets, out_dtype=torch.float32, c=None):
-    """C[M, N] = per-group A . B_g^T with block scales (float32 or bf16 output)."""
-    M, K, G, N = _gemm_operands(aq, as_, bq, bs, offsets)
+def grouped_gemm_fp8_blockscaled(aq, as_, bq, bs, offsets, out_dtype=torch.float32, c=None, a_row=None):
+    """C[M, N] = per-group A . B_g^T with block scales (float32 or bf16 output).
+    a_row (int32 [M]), if given, gathers row m of A from aq[a_row[m]]."""
+    M, K, G, N, A = _gemm_operands(aq, as_, bq, bs, offsets, a_row)
     c = _out(c, "c", (M, N), out_dtype, aq.device)
     _check("grouped_gemm_fp8_blockscaled", lib.grouped_gemm_fp8_blockscaled(
-        _p(aq), _p(as_), _p(bq), _p(bs), _p(offsets), G, M, N, K, _p(c), _dtype_code(c),
+        _p(aq), _p(as_), _p(a_row), A, _p(bq), _p(bs), _p(offsets), G, M, N, K, _p(c), _dtype_code(c),
         _stream()))
     return c
 
 
-def grouped_gemm_fp8_swiglu(aq, as_, bq, bs, offsets, hq=None, hs=None):
-    """Gate|up GEMM with fused SwiGLU + 1x128 quantisation -> (hq [M, I], hs [M, I/128])."""
-    M, K, G, N = _gemm_operands(aq, as_, bq, bs, offsets)
+def grouped_gemm_fp8_swiglu(aq, as_, bq, bs, offsets, hq=None, hs=None, a_row=None):
+    """Gate|up GEMM with fused SwiGLU + 1x128 quantisation -> (hq [M, I], hs [M, I/128]).
+    a_row (int32 [M]), if given, gathers row m of A from aq[a_row[m]]."""
+    M, K, G, N, A = _gemm_operands(aq, as_, bq, bs, offsets, a_row)
     I = N // 2
     hq = _out(hq, "hq", (M, I), torch.uint8, aq.device)
     hs = _out(hs, "hs", (M, I // 128), torch.float32, aq.device)
     _check("grouped_gemm_fp8_swiglu", lib.grouped_gemm_fp8_swiglu(
-        _p(aq), _p(as_), _p(bq), _p(bs), _p(offsets), G, M, I, K, _p(hq), _p(hs), _stream()))
+        _p(aq), _p(as_), _p(a_row), A, _p(bq), _p(bs), _p(offsets), G, M, I, K, _p(hq), _p(hs), _stream()))
     return hq, hs
 
 

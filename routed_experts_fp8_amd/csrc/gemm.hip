@@ -31,6 +31,10 @@
 //    multiplied.  LDS rows are 128 bytes with a 16-byte XOR swizzle (applied
 //    on the global side, since the DMA fixes lane -> LDS address), so the
 //    32-byte operand reads spread over the banks.
+//  * Optional row gather: row m of the grouped operand can be row a_row[m]
+//    of aq / as (the permutation's token index), so the permuted copy of
+//    the activations never has to be written; the indices only change the
+//    per-lane load offsets of the activation slices and scales.
 //  * Ragged groups: token rows past the group's end are clamped on load and
 //    never stored; 16-row instruction tiles past the end are skipped, so a
 //    group of M_g rows costs ceil(M_g / 16) tiles of matrix work.
@@ -135,9 +139,9 @@ __device__ __forceinline__ v8i lds_operand(const uint8_t* rows16, uint32_t lane_
 
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
-    const uint8_t* __restrict__ aq, const float* __restrict__ as, const uint8_t* __restrict__ bq,
-    const float* __restrict__ bs, const int* __restrict__ offsets, int G, int N, int K, int n_tiles,
-    int wg_per_xcd, void* __restrict__ out, float* __restrict__ hs_out) {
+    const uint8_t* __restrict__ aq, const float* __restrict__ as, const int* __restrict__ a_row, int a_rows,
+    const uint8_t* __restrict__ bq, const float* __restrict__ bs, const int* __restrict__ offsets, int G,
+    int N, int K, int n_tiles, int wg_per_xcd, void* __restrict__ out, float* __restrict__ hs_out) {
   constexpr bool kFused = MODE == OUT_SWIGLU;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages * kStageBytes];
   __shared__ int2 sTile[kMaxTilesPerWG];  // {g | n_tile << 10 | rows_valid << 21, row0}
@@ -233,10 +237,22 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
     const int wd = __builtin_amdgcn_readfirstlane(e.x);
     const int row0 = __builtin_amdgcn_readfirstlane(e.y);
     const int g = wd & 1023, n_tile = (wd >> 10) & 2047, rows_valid = wd >> 21;
-    ia_base = aq + (int64_t)row0 * K;
+    // activation rows: row0 + r of the grouped operand, or aq[a_row[row0 + r]]
+    // when gathering (indices clamped into [0, a_rows); the host bounds
+    // a_rows * K by 2^32 so the 32-bit offsets hold)
+    if (a_row != nullptr) {
+      ia_base = aq;
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
-      ia_off[j] = (uint32_t)(min((a_slice0 + j) * 8 + rsub, rows_valid - 1) * K + c16 * 16);
+      for (int j = 0; j < 3; ++j) {
+        const int src = min(max(a_row[row0 + min((a_slice0 + j) * 8 + rsub, rows_valid - 1)], 0), a_rows - 1);
+        ia_off[j] = (uint32_t)src * (uint32_t)K + (uint32_t)(c16 * 16);
+      }
+    } else {
+      ia_base = aq + (int64_t)row0 * K;
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        ia_off[j] = (uint32_t)(min((a_slice0 + j) * 8 + rsub, rows_valid - 1) * K + c16 * 16);
+    }
     const uint8_t* bq_g = bq + (int64_t)g * N * K;
     if (kFused) {
       // waves 0-3 fetch gate block n_tile, waves 4-7 the matching up block
@@ -249,9 +265,17 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) ib_off[j] = (uint32_t)(min((w * 4 + j) * 8 + rsub, last) * K + c16 * 16);
     }
-    if (w < 7) {
-      is_base = reinterpret_cast<const uint8_t*>(as + (int64_t)row0 * KB);
-      is_off = (uint32_t)(min((w - 4) * 64 + lane, rows_valid - 1) * KB * 4);
+    if (w < 4) {
+      // no scale load
+    } else if (w < 7) {
+      const int t = min((w - 4) * 64 + lane, rows_valid - 1);
+      if (a_row != nullptr) {
+        is_base = reinterpret_cast<const uint8_t*>(as);
+        is_off = (uint32_t)min(max(a_row[row0 + t], 0), a_rows - 1) * (uint32_t)(KB * 4);
+      } else {
+        is_base = reinterpret_cast<const uint8_t*>(as + (int64_t)row0 * KB);
+        is_off = (uint32_t)(t * KB * 4);
+      }
     } else {
       const int blkA = kFused ? n_tile : 2 * n_tile;
       const int blkB = kFused ? I / 128 + n_tile : min(2 * n_tile + 1, nblk - 1);
@@ -433,9 +457,9 @@ int device_cu_count() {
 }
 
 template <int MODE>
-moe_status launch_gemm(const uint8_t* aq, const float* as, const uint8_t* bq, const float* bs,
-                       const int* offsets, int G, int64_t M, int N, int K, void* out, float* hs,
-                       hipStream_t st, const char* what) {
+moe_status launch_gemm(const uint8_t* aq, const float* as, const int* a_row, int64_t a_rows,
+                       const uint8_t* bq, const float* bs, const int* offsets, int G, int64_t M, int N,
+                       int K, void* out, float* hs, hipStream_t st, const char* what) {
   const int n_tiles = MODE == OUT_SWIGLU ? (N / 2) / 128 : (N + kBN - 1) / kBN;
   if (n_tiles > kMaxNTiles) return fail(MOE_ERR_UNSUPPORTED, "%s: N=%d too large", what, N);
   // Upper bound on the m-tiles: sum_g ceil(M_g / BM) <= floor(M / BM) + G, and
@@ -459,12 +483,13 @@ moe_status launch_gemm(const uint8_t* aq, const float* as, const uint8_t* bq, co
     if (wg_per_xcd > per_xcd) wg_per_xcd = per_xcd;
   }
   grouped_gemm_kernel<MODE><<<(unsigned)(8 * wg_per_xcd), kThreads, 0, st>>>(
-      aq, as, bq, bs, offsets, G, N, K, n_tiles, (int)wg_per_xcd, out, hs);
+      aq, as, a_row, (int)a_rows, bq, bs, offsets, G, N, K, n_tiles, (int)wg_per_xcd, out, hs);
   return after_launch(what, st);
 }
 
-moe_status check_gemm_args(const uint8_t* aq, const float* as, const uint8_t* bq, const float* bs,
-                           const int32_t* offsets, int32_t G, int64_t M, int32_t N, int32_t K) {
+moe_status check_gemm_args(const uint8_t* aq, const float* as, const int32_t* a_row, int64_t a_rows,
+                           const uint8_t* bq, const float* bs, const int32_t* offsets, int32_t G,
+                           int64_t M, int32_t N, int32_t K) {
   MOE_REQUIRE(G >= 1 && M >= 0 && N > 0 && K > 0, MOE_ERR_SHAPE, "G=%d M=%lld N=%d K=%d", G,
               (long long)M, N, K);
   MOE_REQUIRE(G <= kMaxGroups, MOE_ERR_UNSUPPORTED, "G=%d > %d", G, kMaxGroups);
@@ -477,6 +502,12 @@ moe_status check_gemm_args(const uint8_t* aq, const float* as, const uint8_t* bq
   MOE_REQUIRE(aq && as && bq && bs, MOE_ERR_NULL, "aq, as, bq and bs are required");
   MOE_REQUIRE(aligned(aq, 16) && aligned(bq, 16) && aligned(as, 4) && aligned(bs, 4), MOE_ERR_ALIGN,
               "aq and bq need 16-byte alignment, scales 4-byte");
+  if (a_row) {
+    MOE_REQUIRE(aligned(a_row, 4), MOE_ERR_ALIGN, "a_row needs 4-byte alignment");
+    MOE_REQUIRE(a_rows >= 1, MOE_ERR_SHAPE, "a_rows=%lld must be positive with a_row", (long long)a_rows);
+    MOE_REQUIRE(a_rows * (int64_t)K <= (1LL << 32), MOE_ERR_UNSUPPORTED,
+                "gathered operand of %lld x %d bytes exceeds 4 GiB", (long long)a_rows, K);
+  }
   return MOE_OK;
 }
 
@@ -486,35 +517,37 @@ moe_status check_gemm_args(const uint8_t* aq, const float* as, const uint8_t* bq
 using namespace moefp8;
 
 extern "C" moe_status grouped_gemm_fp8_blockscaled(const uint8_t* aq, const float* as,
+                                                   const int32_t* a_row, int64_t a_rows,
                                                    const uint8_t* bq, const float* bs,
                                                    const int32_t* group_offsets, int32_t G,
                                                    int64_t M, int32_t N, int32_t K, void* c,
                                                    moe_dtype c_dtype, void* stream) {
   clear_detail();
   MOE_REQUIRE(c_dtype == MOE_F32 || c_dtype == MOE_BF16, MOE_ERR_UNSUPPORTED, "c_dtype %d", (int)c_dtype);
-  moe_status stt = check_gemm_args(aq, as, bq, bs, group_offsets, G, M, N, K);
+  moe_status stt = check_gemm_args(aq, as, a_row, a_rows, bq, bs, group_offsets, G, M, N, K);
   if (stt != MOE_OK || M == 0) return stt;
   MOE_REQUIRE(c, MOE_ERR_NULL, "c is required");
   MOE_REQUIRE(aligned(c, 16), MOE_ERR_ALIGN, "c needs 16-byte alignment");
   hipStream_t st = as_stream(stream);
   if (c_dtype == MOE_F32)
-    return launch_gemm<OUT_F32>(aq, as, bq, bs, group_offsets, G, M, N, K, c, nullptr, st,
+    return launch_gemm<OUT_F32>(aq, as, a_row, a_rows, bq, bs, group_offsets, G, M, N, K, c, nullptr, st,
                                 "grouped_gemm_fp8_blockscaled");
-  return launch_gemm<OUT_BF16>(aq, as, bq, bs, group_offsets, G, M, N, K, c, nullptr, st,
+  return launch_gemm<OUT_BF16>(aq, as, a_row, a_rows, bq, bs, group_offsets, G, M, N, K, c, nullptr, st,
                                "grouped_gemm_fp8_blockscaled");
 }
 
-extern "C" moe_status grouped_gemm_fp8_swiglu(const uint8_t* aq, const float* as, const uint8_t* bq,
-                                              const float* bs, const int32_t* group_offsets,
-                                              int32_t G, int64_t M, int32_t I, int32_t K,
-                                              uint8_t* hq, float* hs, void* stream) {
+extern "C" moe_status grouped_gemm_fp8_swiglu(const uint8_t* aq, const float* as, const int32_t* a_row,
+                                              int64_t a_rows, const uint8_t* bq, const float* bs,
+                                              const int32_t* group_offsets, int32_t G, int64_t M,
+                                              int32_t I, int32_t K, uint8_t* hq, float* hs,
+                                              void* stream) {
   clear_detail();
   MOE_REQUIRE(I > 0 && I % 128 == 0, MOE_ERR_SHAPE, "I=%d must be a positive multiple of 128", I);
-  moe_status stt = check_gemm_args(aq, as, bq, bs, group_offsets, G, M, 2 * I, K);
+  moe_status stt = check_gemm_args(aq, as, a_row, a_rows, bq, bs, group_offsets, G, M, 2 * I, K);
   if (stt != MOE_OK || M == 0) return stt;
   MOE_REQUIRE(hq && hs, MOE_ERR_NULL, "hq and hs are required");
   MOE_REQUIRE(aligned(hq, 16) && aligned(hs, 4), MOE_ERR_ALIGN, "hq needs 16-byte alignment");
   hipStream_t st = as_stream(stream);
-  return launch_gemm<OUT_SWIGLU>(aq, as, bq, bs, group_offsets, G, M, 2 * I, K, hq, hs, st,
+  return launch_gemm<OUT_SWIGLU>(aq, as, a_row, a_rows, bq, bs, group_offsets, G, M, 2 * I, K, hq, hs, st,
                                  "grouped_gemm_fp8_swiglu");
 }

@@ -5,9 +5,9 @@ Dataflow ([DSV3-MOE] shared + routed experts, sigmoid top-K with bias, no
 dropping; [PANGU-MOGE] grouped softmax routing; [DSV3-FP8] / [KANANA-FP8]
 fine-grained FP8):
 
-  moe_route -> quant_act_1x128_e4m3(x) -> moe_permute (expert-grouped rows of
-  the FP8 codes) -> grouped_gemm_fp8_swiglu (gate|up GEMM, SwiGLU and 1x128
-  quantisation fused) -> grouped_gemm_fp8_blockscaled (down projection,
+  moe_route -> quant_act_1x128_e4m3(x) -> moe_permute (index maps) ->
+  grouped_gemm_fp8_swiglu (expert-grouped rows gathered from x's FP8 codes
+  through src_token; gate|up GEMM, SwiGLU and 1x128 quantisation fused) -> grouped_gemm_fp8_blockscaled (down projection,
   float32) -> [shared expert: the same two GEMMs with one group over the
   unpermuted tokens] -> moe_combine (gate-weighted sum + shared, bf16).
 
@@ -49,8 +49,7 @@ class MoEForward:
             idx=e((T, K), torch.int32), gate=e((T, K), torch.float32),
             xq=e((T, H), torch.uint8), xs=e((T, H // 128), torch.float32),
             offsets=e((E + 1,), torch.int32), dst_row=e((T, K), torch.int32),
-            src_token=e((M,), torch.int32), aq=e((M, H), torch.uint8),
-            as_=e((M, H // 128), torch.float32),
+            src_token=e((M,), torch.int32),
             hq=e((M, I), torch.uint8), hs=e((M, I // 128), torch.float32),
             c2=e((M, H), torch.float32), y=e((T, H), torch.bfloat16),
             ws=e((L.moe_permute_workspace_size(T, K, E),), torch.uint8),
@@ -69,11 +68,11 @@ class MoEForward:
             if not fused:
                 self.buf["sc1"] = e((T, 2 * shared_I), torch.float32)
 
-    def _ffn(self, aq, as_, offsets, w13q, w13s, w2q, w2s, hq, hs, c2, c1, mark):
+    def _ffn(self, aq, as_, offsets, w13q, w13s, w2q, w2s, hq, hs, c2, c1, mark, a_row=None):
         if self.fused:
-            L.grouped_gemm_fp8_swiglu(aq, as_, w13q, w13s, offsets, hq=hq, hs=hs)
+            L.grouped_gemm_fp8_swiglu(aq, as_, w13q, w13s, offsets, hq=hq, hs=hs, a_row=a_row)
         else:
-            L.grouped_gemm_fp8_blockscaled(aq, as_, w13q, w13s, offsets, c=c1)
+            L.grouped_gemm_fp8_blockscaled(aq, as_, w13q, w13s, offsets, c=c1, a_row=a_row)
             L.swiglu(c1, hq=hq, hs=hs)
         mark("gemm1")
         L.grouped_gemm_fp8_blockscaled(hq, hs, w2q, w2s, offsets, c=c2)
@@ -105,12 +104,13 @@ class MoEForward:
                 self._ffn(b["xq"], b["xs"], b["one_group"], w["sw13q"], w["sw13s"], w["sw2q"], w["sw2s"],
                           b["shq"], b["shs"], b["sc2"], b.get("sc1"), lambda n: None)
             shared = b["sc2"]
-        L.moe_permute(b["idx"], self.E, b["xq"], b["xs"], workspace=b["ws"],
-                      out=dict(offsets=b["offsets"], dst_row=b["dst_row"], src_token=b["src_token"],
-                               aq=b["aq"], **{"as": b["as_"]}))
+        # index maps only: GEMM1 gathers its rows from x's codes through
+        # src_token, so no permuted copy of the activations is written
+        L.moe_permute(b["idx"], self.E, workspace=b["ws"],
+                      out=dict(offsets=b["offsets"], dst_row=b["dst_row"], src_token=b["src_token"]))
         mark("permute")
-        self._ffn(b["aq"], b["as_"], b["offsets"], w["w13q"], w["w13s"], w["w2q"], w["w2s"],
-                  b["hq"], b["hs"], b["c2"], b.get("c1"), mark)
+        self._ffn(b["xq"], b["xs"], b["offsets"], w["w13q"], w["w13s"], w["w2q"], w["w2s"],
+                  b["hq"], b["hs"], b["c2"], b.get("c1"), mark, a_row=b["src_token"])
         if self.shared_I and self.side is None:
             self._ffn(b["xq"], b["xs"], b["one_group"], w["sw13q"], w["sw13s"], w["sw2q"], w["sw2s"],
                       b["shq"], b["shs"], b["sc2"], b.get("sc1"), lambda n: mark("shared_" + n))

@@ -94,18 +94,23 @@ def test_permute_errors():
 
 def test_gemm_errors():
     f = L.lib.grouped_gemm_fp8_blockscaled
-    assert f(P, P, P, P, P, 4, 64, 100, 128, P, 0, S) == SHAPE
-    assert f(P, P, P, P, P, 4, 64, 128, 130, P, 0, S) == SHAPE
-    assert f(P, P, P, P, P, 2048, 64, 128, 128, P, 0, S) == UNSUP
-    assert f(P, P, P, P, P, 0, 64, 128, 128, P, 0, S) == SHAPE
-    assert f(P, P, P, P, N0, 4, 64, 128, 128, P, 0, S) == NULL
-    assert f(P, P, P, P, P, 4, 64, 128, 128, N0, 0, S) == NULL
-    assert f(PM, P, P, P, P, 4, 64, 128, 128, P, 0, S) == ALIGN
-    assert f(P, P, P, P, P, 4, 64, 128, 128, P, 5, S) == UNSUP
-    assert f(N0, N0, N0, N0, P, 4, 0, 128, 128, N0, 0, S) == OK                    # M = 0
+    assert f(P, P, N0, 0, P, P, P, 4, 64, 100, 128, P, 0, S) == SHAPE
+    assert f(P, P, N0, 0, P, P, P, 4, 64, 128, 130, P, 0, S) == SHAPE
+    assert f(P, P, N0, 0, P, P, P, 2048, 64, 128, 128, P, 0, S) == UNSUP
+    assert f(P, P, N0, 0, P, P, P, 0, 64, 128, 128, P, 0, S) == SHAPE
+    assert f(P, P, N0, 0, P, P, N0, 4, 64, 128, 128, P, 0, S) == NULL
+    assert f(P, P, N0, 0, P, P, P, 4, 64, 128, 128, N0, 0, S) == NULL
+    assert f(PM, P, N0, 0, P, P, P, 4, 64, 128, 128, P, 0, S) == ALIGN
+    assert f(P, P, N0, 0, P, P, P, 4, 64, 128, 128, P, 5, S) == UNSUP
+    assert f(N0, N0, N0, 0, N0, N0, P, 4, 0, 128, 128, N0, 0, S) == OK           # M = 0
+    # row gather: misaligned index array, no source rows, source above 4 GiB
+    assert f(P, P, ctypes.c_void_p(0x10002), 16, P, P, P, 4, 64, 128, 128, P, 0, S) == ALIGN
+    assert f(P, P, P, 0, P, P, P, 4, 64, 128, 128, P, 0, S) == SHAPE
+    assert f(P, P, P, 1 << 26, P, P, P, 4, 64, 128, 128, P, 0, S) == UNSUP
     g = L.lib.grouped_gemm_fp8_swiglu
-    assert g(P, P, P, P, P, 4, 64, 100, 128, P, P, S) == SHAPE
-    assert g(P, P, P, P, P, 4, 64, 128, 128, P, N0, S) == NULL
+    assert g(P, P, N0, 0, P, P, P, 4, 64, 100, 128, P, P, S) == SHAPE
+    assert g(P, P, N0, 0, P, P, P, 4, 64, 128, 128, P, N0, S) == NULL
+    assert g(P, P, P, 0, P, P, P, 4, 64, 128, 128, P, P, S) == SHAPE
 
 
 def test_swiglu_combine_transpose_errors():

@@ -72,13 +72,17 @@ def _oracle_rows(x_np, src_o, rows):
     return O.quant_act_1x128(x_np[src_o[rows]])
 
 
-def _check_gemm1(cfg, d, perm, w, x_np, po, groups):
+def _check_gemm1(cfg, d, perm, w, x_np, po, groups, xq, xs):
     """Fused gate|up GEMM + SwiGLU + quantisation at full size (GPU launch as
-    in the bench) on sampled rows of sampled experts, against the oracle's
-    own operands and its own quantised weights."""
+    in the bench: rows gathered from x's codes through src_token) on sampled
+    rows of sampled experts, against the oracle's own operands and its own
+    quantised weights; the launch on the permuted copy gives the same bits."""
     off = po["offsets"]
     rows = _sample_rows(off, groups)
-    hq, hs = R.grouped_gemm_fp8_swiglu(perm["aq"], perm["as"], w["w13q"], w["w13s"], perm["offsets"])
+    hq, hs = R.grouped_gemm_fp8_swiglu(xq, xs, w["w13q"], w["w13s"], perm["offsets"], a_row=perm["src_token"])
+    hq2, hs2 = R.grouped_gemm_fp8_swiglu(perm["aq"], perm["as"], w["w13q"], w["w13s"], perm["offsets"])
+    assert torch.equal(hq, hq2) and torch.equal(hs, hs2)
+    del hq2, hs2
     hq, hs = np_(hq), np_(hs)
     grp = np.searchsorted(off, rows, side="right") - 1
     for g in np.unique(grp):
@@ -150,7 +154,7 @@ def test_fullsize_layer_pieces(key):
     nz = order[counts[order] > 0]
     groups = sorted(set([int(nz[0]), int(nz[-1]), int(nz[len(nz) // 2])] +
                         RNG.choice(nz, 3, replace=False).tolist()))
-    n_rows = _check_gemm1(cfg, d, perm, w, x_np, po, groups)
+    n_rows = _check_gemm1(cfg, d, perm, w, x_np, po, groups, xq, xs)
 
     def w2_oracle(g):
         q2, s2 = O.quant_weight_128x128(np_(d["w2"][g:g + 1]))

@@ -266,6 +266,42 @@ def test_grouped_gemm_many_tiles_short_k(K):
     hq, hs = R.grouped_gemm_fp8_swiglu(*args)
     hq2, hs2 = R.swiglu(c)
     assert np.array_equal(np_(hq), np_(hq2)) and np.array_equal(np_(hs), np_(hs2))
+    # the same operand gathered from a shuffled source through a row index:
+    # identical bits, tile switches now reloading gathered row offsets
+    perm = RNG.permutation(M)
+    src_q, src_s = np.empty_like(aq), np.empty_like(as_)
+    src_q[perm], src_s[perm] = aq, as_
+    a_row = to_dev(perm.astype(np.int32))
+    cg = R.grouped_gemm_fp8_blockscaled(to_dev(src_q), to_dev(src_s), args[2], args[3], args[4], a_row=a_row)
+    assert torch.equal(cg, c)
+    hg, hsg = R.grouped_gemm_fp8_swiglu(to_dev(src_q), to_dev(src_s), args[2], args[3], args[4], a_row=a_row)
+    assert torch.equal(hg, hq) and torch.equal(hsg, hs)
+
+
+@pytest.mark.parametrize("K", [384, 7168])
+def test_grouped_gemm_row_gather(K):
+    """Rows gathered through an index with repeats (several grouped rows read
+    one source row, as tokens do across their top-K experts): equal to the
+    GEMM on the explicitly gathered operand, and within tolerance of the
+    oracle on it.  K = 7168 runs one tile per workgroup, K = 384 the
+    persistent tile walk."""
+    sizes = [5, 0, 17, 1, 300, 161]
+    G, M, N, A = len(sizes), sum(sizes), 256, 97
+    src_q, src_s, bq, bs, off = _gemm_problem([A] + [0] * (G - 1), N, K, RNG)
+    a_row_np = RNG.integers(0, A, M).astype(np.int32)
+    off = rand_offsets(RNG, sizes)
+    aq, as_ = src_q[a_row_np], src_s[a_row_np]
+    w = [to_dev(v) for v in (bq, bs, off)]
+    c = R.grouped_gemm_fp8_blockscaled(to_dev(src_q), to_dev(src_s), *w, a_row=to_dev(a_row_np))
+    assert torch.equal(c, R.grouped_gemm_fp8_blockscaled(to_dev(aq), to_dev(as_), *w))
+    C, Mag = O.grouped_gemm(aq, as_, bq, bs, off)
+    assert_gemm_close(np_(c), C, Mag)
+    if K == 384:
+        bq2, bs2 = O.quant_weight_128x128((RNG.standard_normal((G, 2 * N, K)) * 0.02).astype(np.float32))
+        w2 = [to_dev(v) for v in (bq2, bs2, off)]
+        hq, hs = R.grouped_gemm_fp8_swiglu(to_dev(src_q), to_dev(src_s), *w2, a_row=to_dev(a_row_np))
+        hq2, hs2 = R.grouped_gemm_fp8_swiglu(to_dev(aq), to_dev(as_), *w2)
+        assert torch.equal(hq, hq2) and torch.equal(hs, hs2)
 
 
 def test_grouped_gemm_exact_integers():
