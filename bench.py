@@ -273,11 +273,11 @@ def main():
                                                TFLOPs=sf1 / stage_ms["shared_gemm1"] / 1e9)
             gemm["shared_gemm2"] = dict(ms=stage_ms["shared_gemm2"], TFLOPs=sf2 / stage_ms["shared_gemm2"] / 1e9)
             all_gemm_ms += stage_ms["shared_gemm1"] + stage_ms["shared_gemm2"]
-        else:  # on the side stream, overlapped with permute and the routed GEMMs:
-            # the GEMM phase runs from the end of quant_act to the join
+        else:  # on the side stream, overlapped with routing, permutation and the
+            # routed GEMMs: the GEMM phase runs from the end of quant_act to the join
             gemm["shared_expert"] = dict(overlapped=True, flops=sf1 + sf2,
                                          join_wait_ms=stage_ms.get("shared_join", 0.0))
-            all_gemm_ms += stage_ms.get("shared_join", 0.0) + stage_ms["permute"]
+            all_gemm_ms += stage_ms.get("shared_join", 0.0) + stage_ms["permute"] + stage_ms["route"]
         all_gemm_flops += sf1 + sf2
     gemm["all_grouped_gemms"] = dict(ms=all_gemm_ms, TFLOPs=all_gemm_flops / all_gemm_ms / 1e9,
                                      frac_mfma=all_gemm_flops / all_gemm_ms / 1e9 / FP8_PEAK_TFLOPS)

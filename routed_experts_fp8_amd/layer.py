@@ -1,15 +1,19 @@
 """The routed-expert FP8 MoE FFN layer forward, as a sequence of library
-calls on one stream (no host synchronisation inside).
+calls (no host synchronisation inside).
 
 Dataflow ([DSV3-MOE] shared + routed experts, sigmoid top-K with bias, no
 dropping; [PANGU-MOGE] grouped softmax routing; [DSV3-FP8] / [KANANA-FP8]
 fine-grained FP8):
 
-  moe_route -> quant_act_1x128_e4m3(x) -> moe_permute (index maps) ->
+  quant_act_1x128_e4m3(x) -> moe_route -> moe_permute (index maps) ->
   grouped_gemm_fp8_swiglu (expert-grouped rows gathered from x's FP8 codes
-  through src_token; gate|up GEMM, SwiGLU and 1x128 quantisation fused) -> grouped_gemm_fp8_blockscaled (down projection,
-  float32) -> [shared expert: the same two GEMMs with one group over the
-  unpermuted tokens] -> moe_combine (gate-weighted sum + shared, bf16).
+  through src_token; gate|up GEMM, SwiGLU and 1x128 quantisation fused) ->
+  grouped_gemm_fp8_blockscaled (down projection, float32) -> moe_combine
+  (gate-weighted sum + shared expert, bf16).
+
+The shared expert (the same two GEMMs, one group over the unpermuted
+tokens) runs on a side stream from the quantisation on and joins before the
+combine.
 
 Weights are quantised ahead of the forward (``quantize_weights``), as in
 training where quantisation runs once per optimizer step for all experts.
@@ -85,30 +89,44 @@ class MoEForward:
         marked; "shared_join" marks the caller's stream waiting for them."""
         mark = on_stage or (lambda name: None)
         b, w, r = self.buf, self.w, self.route
-        if r["mode"] == "sigmoid_bias":
-            L.moe_route(logits, bias, self.K, "sigmoid_bias", normalize=r.get("normalize", True),
-                        topk_idx=b["idx"], topk_gate=b["gate"])
-        else:
-            L.moe_route(logits, None, self.K, "softmax_grouped", n_groups=r["n_groups"],
-                        k_per_group=r["k_per_group"], topk_idx=b["idx"], topk_gate=b["gate"])
-        mark("route")
-        L.quant_act_1x128_e4m3(x, q=b["xq"], scale=b["xs"])
-        mark("quant_act")
         shared = None
-        if self.shared_I and self.side is not None:
-            # forked as soon as x's codes exist: the permutation and the routed
-            # GEMM1 then fill the CUs the shared GEMMs' last partial wave of
-            # workgroups leaves idle
-            self.side.wait_stream(torch.cuda.current_stream())
-            with torch.cuda.stream(self.side):
-                self._ffn(b["xq"], b["xs"], b["one_group"], w["sw13q"], w["sw13s"], w["sw2q"], w["sw2s"],
-                          b["shq"], b["shs"], b["sc2"], b.get("sc1"), lambda n: None)
-            shared = b["sc2"]
-        # index maps only: GEMM1 gathers its rows from x's codes through
-        # src_token, so no permuted copy of the activations is written
-        L.moe_permute(b["idx"], self.E, workspace=b["ws"],
-                      out=dict(offsets=b["offsets"], dst_row=b["dst_row"], src_token=b["src_token"]))
-        mark("permute")
+
+        def route():
+            if r["mode"] == "sigmoid_bias":
+                L.moe_route(logits, bias, self.K, "sigmoid_bias", normalize=r.get("normalize", True),
+                            topk_idx=b["idx"], topk_gate=b["gate"])
+            else:
+                L.moe_route(logits, None, self.K, "softmax_grouped", n_groups=r["n_groups"],
+                            k_per_group=r["k_per_group"], topk_idx=b["idx"], topk_gate=b["gate"])
+            mark("route")
+
+        def quant():
+            L.quant_act_1x128_e4m3(x, q=b["xq"], scale=b["xs"])
+            mark("quant_act")
+
+        def fork():  # shared expert on the side stream
+            nonlocal shared
+            if self.shared_I and self.side is not None:
+                self.side.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(self.side):
+                    self._ffn(b["xq"], b["xs"], b["one_group"], w["sw13q"], w["sw13s"], w["sw2q"], w["sw2s"],
+                              b["shq"], b["shs"], b["sc2"], b.get("sc1"), lambda n: None)
+                shared = b["sc2"]
+
+        def permute():
+            # index maps only: GEMM1 gathers its rows from x's codes through
+            # src_token, so no permuted copy of the activations is written
+            L.moe_permute(b["idx"], self.E, workspace=b["ws"],
+                          out=dict(offsets=b["offsets"], dst_row=b["dst_row"], src_token=b["src_token"]))
+            mark("permute")
+
+        # The shared expert needs only x's codes: it is forked first, and the
+        # routing, permutation and routed GEMM1 fill the CUs its last partial
+        # wave of workgroups leaves idle.
+        quant()
+        fork()
+        route()
+        permute()
         self._ffn(b["xq"], b["xs"], b["offsets"], w["w13q"], w["w13s"], w["w2q"], w["w2s"],
                   b["hq"], b["hs"], b["c2"], b.get("c1"), mark, a_row=b["src_token"])
         if self.shared_I and self.side is None:
