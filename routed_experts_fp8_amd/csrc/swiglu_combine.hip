@@ -9,8 +9,8 @@
 // combine ([DSV3-MOE], shared + routed experts): out[t] = bf16(sum_k
 // gate[t,k] * y_perm[dst_row[t,k]] + shared[t]), summed in slot order in
 // binary32 (fixed order, so the result is reproducible).  One workgroup per
-// token; each thread carries 4 columns and keeps K + 1 independent 16-byte
-// loads in flight.
+// token; each thread carries 4 columns and keeps up to 8 independent 16-byte
+// loads in flight (non-temporal: every expert output is read once).
 #include "device_common.h"
 #include "host_common.h"
 
@@ -51,29 +51,56 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ g
   }
 }
 
+// Slots are taken 8 at a time: the rows and gates of a batch are
+// wave-uniform (scalar loads), the batch's 16-byte loads are all issued
+// before the first add, and the adds then run in slot order.  For K <= 8 (one
+// batch) the rows and gates are read once per token, outside the column loop.
+constexpr int kCombineBatch = 8;
+
+template <bool kOneBatch>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y_perm,
                                                       const int* __restrict__ dst_row,
                                                       const float* __restrict__ gate,
                                                       const float* __restrict__ shared, int K,
                                                       int H, uint16_t* __restrict__ out) {
   const int64_t t = blockIdx.x;
+  const float* row[kCombineBatch];
+  float g[kCombineBatch];
+  auto load_batch = [&](int k0) {
+#pragma unroll
+    for (int j = 0; j < kCombineBatch; ++j) {
+      if (k0 + j < K) {
+        row[j] = y_perm + (int64_t)dst_row[t * K + k0 + j] * H;
+        g[j] = gate[t * K + k0 + j];
+      }
+    }
+  };
+  if (kOneBatch) load_batch(0);
   for (int c = 4 * threadIdx.x; c < H; c += 4 * blockDim.x) {
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int k = 0; k < K; ++k) {
-      const float g = gate[t * K + k];
-      const int64_t r = dst_row[t * K + k];
-      const float4 y = *reinterpret_cast<const float4*>(y_perm + r * H + c);
-      acc[0] = acc[0] + g * y.x;
-      acc[1] = acc[1] + g * y.y;
-      acc[2] = acc[2] + g * y.z;
-      acc[3] = acc[3] + g * y.w;
+    for (int k0 = 0; k0 < K; k0 += kCombineBatch) {
+      if (!kOneBatch) load_batch(k0);
+      u32x4 y[kCombineBatch];
+#pragma unroll
+      for (int j = 0; j < kCombineBatch; ++j)
+        if (k0 + j < K) y[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row[j] + c));
+#pragma unroll
+      for (int j = 0; j < kCombineBatch; ++j) {
+        if (k0 + j < K) {
+          acc[0] = acc[0] + g[j] * __uint_as_float(y[j][0]);
+          acc[1] = acc[1] + g[j] * __uint_as_float(y[j][1]);
+          acc[2] = acc[2] + g[j] * __uint_as_float(y[j][2]);
+          acc[3] = acc[3] + g[j] * __uint_as_float(y[j][3]);
+        }
+      }
+      if (kOneBatch) break;
     }
     if (shared) {
-      const float4 s = *reinterpret_cast<const float4*>(shared + t * H + c);
-      acc[0] = acc[0] + s.x;
-      acc[1] = acc[1] + s.y;
-      acc[2] = acc[2] + s.z;
-      acc[3] = acc[3] + s.w;
+      const u32x4 s4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(shared + t * H + c));
+      acc[0] = acc[0] + __uint_as_float(s4[0]);
+      acc[1] = acc[1] + __uint_as_float(s4[1]);
+      acc[2] = acc[2] + __uint_as_float(s4[2]);
+      acc[3] = acc[3] + __uint_as_float(s4[3]);
     }
     uint2 o;
     o.x = bf16_rne_bits(acc[0]) | (bf16_rne_bits(acc[1]) << 16);
@@ -115,6 +142,9 @@ extern "C" moe_status moe_combine(const float* y_perm, const int32_t* dst_row,
                   aligned(dst_row, 4) && aligned(topk_gate, 4),
               MOE_ERR_ALIGN, "y_perm, shared and out need 16-byte alignment");
   hipStream_t st = as_stream(stream);
-  combine_kernel<<<(unsigned)T, 256, 0, st>>>(y_perm, dst_row, topk_gate, shared, K, H, out_bf16);
+  if (K <= kCombineBatch)
+    combine_kernel<true><<<(unsigned)T, 256, 0, st>>>(y_perm, dst_row, topk_gate, shared, K, H, out_bf16);
+  else
+    combine_kernel<false><<<(unsigned)T, 256, 0, st>>>(y_perm, dst_row, topk_gate, shared, K, H, out_bf16);
   return after_launch("moe_combine", st);
 }
