@@ -132,6 +132,37 @@ def extra_rows(cfg, d, fwd, torch, R, synth, reps=5):
     return out
 
 
+def other_workload_rows(torch, R, synth, names=("moge", "skewed"), reps=5):
+    """GEMM1 (gate|up + SwiGLU, gathered rows) and GEMM2 throughput and the
+    whole layer forward on the other routing workloads, whose GEMM1 sits
+    above the MFMA ridge (compute-bound).  Same kernels and launch as the
+    layer; context rows, not the headline."""
+    out = {}
+    dev = torch.device("cuda:0")
+    for name in names:
+        cfg = synth.get_config(name)
+        T, H, E, I, K = cfg["T"], cfg["H"], cfg["E"], cfg["I"], cfg["K"]
+        d = synth.layer_inputs(cfg, dev, seed=0)
+        w = R.quantize_weights(d["w13"], d["w2"])
+        del d["w13"], d["w2"]
+        fwd = R.MoEForward(T, H, E, I, cfg["route"], w, dev, fused=True)
+        layer_ms = time_op(lambda: fwd(d["x"], d["logits"], d["bias"]), reps, torch)
+        b = fwd.buf
+        g1 = time_op(lambda: R.grouped_gemm_fp8_swiglu(b["xq"], b["xs"], w["w13q"], w["w13s"], b["offsets"],
+                                                         hq=b["hq"], hs=b["hs"], a_row=b["src_token"]), reps, torch)
+        g2 = time_op(lambda: R.grouped_gemm_fp8_blockscaled(b["hq"], b["hs"], w["w2q"], w["w2s"], b["offsets"],
+                                                              c=b["c2"]), reps, torch)
+        M = T * K
+        f1, f2 = gemm_flops(M, 2 * I, H), gemm_flops(M, H, I)
+        out[cfg["name"]] = dict(
+            layer_ms=layer_ms, tokens_per_s=T / (layer_ms / 1e3),
+            gemm1_swiglu=dict(ms=g1, TFLOPs=f1 / g1 / 1e9, frac_mfma=f1 / g1 / 1e9 / FP8_PEAK_TFLOPS),
+            gemm2=dict(ms=g2, TFLOPs=f2 / g2 / 1e9, frac_mfma=f2 / g2 / 1e9 / FP8_PEAK_TFLOPS))
+        del fwd, w, d, b
+        torch.cuda.empty_cache()
+    return out
+
+
 def cpu_baseline(cfg, d, n_experts=2, shared_tokens=128, combine_tokens=256):
     """The oracle as it stands, on a bounded sample of the workload, scaled to
     the full layer: routing, activation quantisation and permutation of all
@@ -292,6 +323,8 @@ def main():
     if not args.no_extra:
         log("extra rows: weight quantisation, block transpose, dgrad")
         extra = extra_rows(cfg, d, fwd, torch, R, synth)
+        log("other workloads: MoGE and skewed-load layers")
+        extra["other_workloads"] = other_workload_rows(torch, R, synth)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle, bounded sample)")
