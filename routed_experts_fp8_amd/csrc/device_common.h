@@ -23,35 +23,54 @@ __device__ __forceinline__ void store16_nt(void* p, const uint4& v) {
 }
 
 // ---------------------------------------------------------------------------
-// E4M3FN encoding (OCP 8-bit float, bias 7, 3 mantissa bits, max 448).
-// Input: finite binary32 with |v| <= 448.  Round to nearest, ties to even,
-// sign kept.  Pure integer work on the binary32 pattern:
-//  * |v| >= 2^-6 (normal E4M3): keep the top 3 mantissa bits with
-//    round-half-even (add 0x7FFFF plus the kept LSB, shift right by 20); the
-//    biased exponent moves from bias 127 to bias 7, i.e. subtract
-//    (127 - 7) << 3 = 0x3C0 from the (exponent << 3 | mantissa) field.  A
-//    mantissa carry rolls into the exponent, which is still correct.
-//  * |v| < 2^-6 (subnormal E4M3, spacing 2^-9): |v| * 2^9 is exact and
-//    rint (half-even) gives the code directly (0..8; 8 is 2^-6 = 0x08).
+// FP8 quantisation: code = RNE_E4M3(clamp(fl32(x / s), -448, 448)).
+//
+// Division.  fl32(x / s) is the correctly rounded quotient.  It is formed
+// with Markstein's FMA correction (P. Markstein, "Computation of elementary
+// functions on the IBM RISC System/6000 processor", IBM J. Res. Dev. 34(1),
+// 1990): with r = RN(1/s) and the faithful quotient q0 = RN(x * r), the
+// residual x - s * q0 is exact in one FMA and RN(q0 + residual * r) equals
+// RN(x / s).  The theorem needs r and the residual free of overflow and
+// underflow; the scales here are fl32(amax / 448), so the correction is used
+// for s >= 2^-100 (r normal, quotients at most ~448) and a direct correctly
+// rounded division otherwise.  A zero quotient takes the sign of x.
+//
+// Encoding.  gfx950's V_CVT_PK_FP8_F32 converts two binary32 values to OCP
+// E4M3FN (bias 7, 3 mantissa bits, max 448) with round to nearest-even,
+// including the subnormal codes; inputs are clamped to +-448 first.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t e4m3_encode(float v) {
-  const uint32_t u = __float_as_uint(v);
-  const uint32_t sign = (u >> 24) & 0x80u;
-  const uint32_t a = u & 0x7fffffffu;
-  const uint32_t normal = ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - 0x3c0u;
-  const uint32_t sub = (uint32_t)__builtin_rintf(fminf(__uint_as_float(a), 0x1p-6f) * 512.0f);
-  return (a < 0x3c800000u ? sub : normal) | sign;
-}
+struct Divider {
+  float s, r;
+  bool direct;  // wave-uniform: some active lane's scale is below 2^-100
+  __device__ __forceinline__ explicit Divider(float s_)
+      : s(s_), r(1.0f / s_), direct(__builtin_amdgcn_ballot_w64(s_ < 0x1p-100f) != 0) {}
+  template <bool kDirect>
+  __device__ __forceinline__ float div(float x) const {
+    if (kDirect) return x / s;
+    const float q0 = x * r;
+    const float e = __builtin_fmaf(-s, q0, x);
+    return __builtin_copysignf(__builtin_fmaf(e, r, q0), x);
+  }
+};
 
 // Scale of a tile or block from its amax: fl32(amax / 448), 1 if amax == 0.
 __device__ __forceinline__ float scale_from_amax(float amax) {
   return amax == 0.0f ? 1.0f : amax / kE4M3Max;
 }
 
-// Code of x under scale s: RNE_E4M3(clamp(fl32(x / s), -448, 448)).
-__device__ __forceinline__ uint32_t quantize(float x, float s) {
-  const float y = fminf(fmaxf(x / s, -kE4M3Max), kE4M3Max);
-  return e4m3_encode(y);
+__device__ __forceinline__ float clamp_e4m3(float y) { return fminf(fmaxf(y, -kE4M3Max), kE4M3Max); }
+
+// Codes of four values under one scale, packed little-endian (x0 in the low
+// byte), as stored in the row-major code arrays.
+template <bool kDirect>
+__device__ __forceinline__ uint32_t quantize4_impl(const Divider& d, float x0, float x1, float x2, float x3) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_e4m3(d.div<kDirect>(x0)), clamp_e4m3(d.div<kDirect>(x1)), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp_e4m3(d.div<kDirect>(x2)), clamp_e4m3(d.div<kDirect>(x3)), w, true);
+  return (uint32_t)w;
+}
+__device__ __forceinline__ uint32_t quantize4(const Divider& d, float x0, float x1, float x2, float x3) {
+  return __builtin_expect(d.direct, 0) ? quantize4_impl<true>(d, x0, x1, x2, x3)
+                                       : quantize4_impl<false>(d, x0, x1, x2, x3);
 }
 
 // ---------------------------------------------------------------------------

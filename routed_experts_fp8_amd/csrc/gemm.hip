@@ -426,12 +426,12 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
         if (j < n_active && mloc < rows_valid) {
           const float amax = fmaxf(fmaxf(sAmax[0][mloc], sAmax[1][mloc]), fmaxf(sAmax[2][mloc], sAmax[3][mloc]));
           const float sc = scale_from_amax(amax);
+          const Divider div(sc);
           const int64_t m = row0 + mloc;
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
             const int col = n_tile * 128 + 32 * wn + 16 * i + 4 * q;
-            const uint32_t wd4 = quantize(acc[i][j][0], sc) | (quantize(acc[i][j][1], sc) << 8) |
-                                 (quantize(acc[i][j][2], sc) << 16) | (quantize(acc[i][j][3], sc) << 24);
+            const uint32_t wd4 = quantize4(div, acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
             *reinterpret_cast<uint32_t*>(hq + m * I + col) = wd4;
           }
           if (wn == 0 && q == 0) hs_out[m * (I / 128) + n_tile] = sc;

@@ -31,18 +31,18 @@ template <> struct Vec<float> {
   }
 };
 
-template <int N>
-__device__ __forceinline__ void store_codes(uint8_t* dst, const uint32_t* c);
+template <int E>
+__device__ __forceinline__ void store_codes(uint8_t* dst, const Divider& d, const float* f);
 template <>
-__device__ __forceinline__ void store_codes<8>(uint8_t* dst, const uint32_t* c) {
+__device__ __forceinline__ void store_codes<8>(uint8_t* dst, const Divider& d, const float* f) {
   uint2 v;
-  v.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-  v.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
+  v.x = quantize4(d, f[0], f[1], f[2], f[3]);
+  v.y = quantize4(d, f[4], f[5], f[6], f[7]);
   *reinterpret_cast<uint2*>(dst) = v;
 }
 template <>
-__device__ __forceinline__ void store_codes<4>(uint8_t* dst, const uint32_t* c) {
-  *reinterpret_cast<uint32_t*>(dst) = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
+__device__ __forceinline__ void store_codes<4>(uint8_t* dst, const Divider& d, const float* f) {
+  *reinterpret_cast<uint32_t*>(dst) = quantize4(d, f[0], f[1], f[2], f[3]);
 }
 
 // ---------------------------------------------------------------------------
@@ -79,10 +79,7 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const T* __restrict__ x,
       amax = group_max<LPT>(amax);  // whole wave participates (uniform control)
       if (v < n_vec) {
         const float s = scale_from_amax(amax);
-        uint32_t c[E];
-#pragma unroll
-        for (int i = 0; i < E; ++i) c[i] = quantize(f[i], s);
-        store_codes<E>(q + v * E, c);
+        store_codes<E>(q + v * E, Divider(s), f);
         if ((threadIdx.x % LPT) == 0) scale[v / LPT] = s;
       }
     }
@@ -132,6 +129,7 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const T* __restrict__
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   const float s = scale_from_amax(amax);
+  const Divider div(s);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const int id = i * 256 + tid;
@@ -139,10 +137,7 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const T* __restrict__
     const int64_t off = gbase + (int64_t)(bi * 128 + r) * cols + bj * 128 + cv * E;
     float f[E];
     Vec<T>::unpack(raw[i], f);
-    uint32_t c[E];
-#pragma unroll
-    for (int k = 0; k < E; ++k) c[k] = quantize(f[k], s);
-    store_codes<E>(q + off, c);
+    store_codes<E>(q + off, div, f);
   }
   if (tid == 0) scale[blk] = s;  // [G, rows/128, cols/128] row-major == blk order
 }

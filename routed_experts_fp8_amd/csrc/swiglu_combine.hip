@@ -43,8 +43,7 @@ __global__ __launch_bounds__(256) void swiglu_kernel(const float* __restrict__ g
     amax = group_max<32>(amax);
     if (ok) {
       const float s = scale_from_amax(amax);
-      const uint32_t w = quantize(h[0], s) | (quantize(h[1], s) << 8) | (quantize(h[2], s) << 16) |
-                         (quantize(h[3], s) << 24);
+      const uint32_t w = quantize4(Divider(s), h[0], h[1], h[2], h[3]);
       *reinterpret_cast<uint32_t*>(hq + m * I + 4 * c4) = w;
       if ((c4 & 31) == 0) hs[m * (I / 128) + c4 / 32] = s;
     }
