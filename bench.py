@@ -163,7 +163,7 @@ def other_workload_rows(torch, R, synth, names=("moge", "skewed"), reps=5):
     return out
 
 
-def cpu_baseline(cfg, d, n_experts=2, shared_tokens=128, combine_tokens=256):
+def cpu_baseline(cfg, d, n_experts=12, shared_tokens=1024, combine_tokens=2048):
     """The oracle as it stands, on a bounded sample of the workload, scaled to
     the full layer: routing, activation quantisation and permutation of all
     tokens; the routed-expert FFN (GEMM1, SwiGLU + quantisation, GEMM2) for
