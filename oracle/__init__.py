@@ -58,6 +58,8 @@ from .permute import permute
 from .gemm import grouped_gemm, grouped_gemm_rows
 from .swiglu import swiglu_quant
 from .combine import combine_ref, combine_fp32_replay
+from .backward import (combine_backward, swiglu_backward, route_backward_sigmoid,
+                       route_backward_softmax, layer_backward)
 from .transpose import block_transpose
 from .layer import layer_forward, layer_forward_dense
 
@@ -67,5 +69,6 @@ __all__ = [
     "quant_weight_128x128", "dequant_act", "dequant_weight", "route_sigmoid_bias",
     "route_softmax_grouped", "imbalance_score", "permute", "grouped_gemm",
     "grouped_gemm_rows", "swiglu_quant", "combine_ref", "combine_fp32_replay",
-    "block_transpose", "layer_forward", "layer_forward_dense",
+    "block_transpose", "layer_forward", "layer_forward_dense", "combine_backward",
+    "swiglu_backward", "route_backward_sigmoid", "route_backward_softmax", "layer_backward",
 ]
