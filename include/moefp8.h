@@ -267,6 +267,72 @@ MOE_API moe_status moe_combine(const float* y_perm, const int32_t* dst_row, cons
 MOE_API moe_status fp8_block_transpose(const uint8_t* q, const float* scale, int32_t G, int32_t rows,
                                int32_t cols, uint8_t* qt, float* scale_t, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Input-side backward.  [KANANA-FP8]: the backward expert GEMMs run in FP8
+ * on the block-transposed forward weights (fp8_block_transpose, then
+ * grouped_gemm_fp8_blockscaled with the transposed copy as B); their inputs
+ * are quantised in 1x128 tiles along the reduction dimension ([DSV3-FP8]).
+ * Gradients pass straight through the FP8 rounding.
+ * ------------------------------------------------------------------------ */
+
+/*
+ * moe_combine_backward -- gradient of the gate-weighted combine
+ * y[t] = sum_k gate[t,k] * y_perm[dst_row[t,k]] (+ shared[t]).   [DSV3-MOE]
+ *
+ *  dy        bf16 [T, H] (raw 16-bit patterns)  upstream gradient
+ *  y_perm    f32  [T*K, H]   the forward's expert outputs (permuted order)
+ *  dst_row   i32  [T, K], topk_gate f32 [T, K]  as in moe_combine
+ *  dq, ds    u8 [T*K, H], f32 [T*K, H/128] (out): fl32(gate[t,k] * dy[t])
+ *            written at row dst_row[t,k], quantised in 1x128 tiles (the FP8
+ *            operand of the down projection's dgrad)
+ *  d_gate    f32  [T, K] (out): <dy[t], y_perm[dst_row[t,k]]>, summed in a
+ *            fixed order (reproducible)
+ *  The shared expert's gradient is dy itself (quantise it with
+ *  quant_act_1x128_e4m3).  H % 128 == 0, 1 <= K <= 16.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED (K > 16), MOE_ERR_ALIGN
+ *         (dy, y_perm 16-byte; dq 8-byte).
+ */
+MOE_API moe_status moe_combine_backward(const uint16_t* dy_bf16, const float* y_perm, const int32_t* dst_row,
+                                const float* topk_gate, int32_t T, int32_t K, int32_t H, uint8_t* dq,
+                                float* ds, float* d_gate, void* stream);
+
+/*
+ * swiglu_backward -- gradient of h = silu(g) * u, [g | u] the float32
+ * gate|up GEMM output, with the result quantised for the gate|up dgrad.
+ *
+ *  gate_up  f32 [M, 2I]  the forward's gate|up output (g = [:, :I], u = [:, I:])
+ *  dh       f32 [M, I]   gradient of h
+ *  dq, ds   u8 [M, 2I], f32 [M, 2I/128] (out): [dg | du] quantised in 1x128
+ *           tiles, with (binary32, s the sigmoid specification of moe_route):
+ *           silu = g*s; dsilu = s*(1 + g*(1 - s)); du = dh*silu; dg = (dh*u)*dsilu
+ *  I % 128 == 0.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN (gate_up, dh 16-byte).
+ */
+MOE_API moe_status swiglu_backward(const float* gate_up, const float* dh, int64_t M, int32_t I, uint8_t* dq,
+                           float* ds, void* stream);
+
+/*
+ * moe_route_backward -- gradient of the gates with respect to the router
+ * logits, through the selected experts only (top-K selection is piecewise
+ * constant; the balancing bias selects but does not weight).
+ *                                                 [DSV3-MOE], [PANGU-MOGE]
+ *  logits    f32 [T, E], topk_idx i32 [T, K]   the forward's inputs / selection
+ *  d_gate    f32 [T, K]   gradient of the gates (moe_combine_backward)
+ *  mode, normalize_topk   as in moe_route (n_groups is not needed)
+ *  d_logits  f32 [T, E] (out), every element written:
+ *    SIGMOID_BIAS: s_k = sigmoid(l_k); dL/ds_k = (d_gate_k - sum_j d_gate_j gate_j) / S
+ *      with S = sum_j s_j when normalised (else d_gate_k); dL/dl = dL/ds_k s_k (1 - s_k)
+ *      at the selected experts, 0 elsewhere.
+ *    SOFTMAX_GROUPED: p = softmax(l) over all E, gate_k = p[topk_idx[k]];
+ *      dL/dl_j = p_j (D_j - sum_k d_gate_k gate_k), D_j = d_gate_k at j = topk_idx[k].
+ *  Evaluated in float64 and rounded once.  K <= 64; topk_idx values outside
+ *  [0, E) contribute nothing.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_ALIGN.
+ */
+MOE_API moe_status moe_route_backward(const float* logits, const int32_t* topk_idx, const float* d_gate,
+                              int32_t T, int32_t E, int32_t K, moe_route_mode mode, int32_t normalize_topk,
+                              float* d_logits, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -39,6 +39,11 @@ _SIGNATURES = {
                            _c_void_p]),
     "fp8_block_transpose": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _i32, _c_void_p, _c_void_p,
                                    _c_void_p]),
+    "moe_combine_backward": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
+                                    _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "swiglu_backward": (_i32, [_c_void_p, _c_void_p, _i64, _i32, _c_void_p, _c_void_p, _c_void_p]),
+    "moe_route_backward": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32,
+                                  _c_void_p, _c_void_p]),
 }
 
 
@@ -214,9 +219,12 @@ def _gemm_operands(aq, as_, bq, bs, offsets, a_row):
 
 
 def grouped_gemm_fp8_blockscaled(aq, as_, bq, bs, offsets, out_dtype=torch.float32, c=None, a_row=None):
-    """C[M, N] = per-group A . B_g^T with block scales (float32 or bf16 output).
+    """C[M, N] = per-group A . B_g^T with block scales (float32 or bf16 output;
+    the type of ``c`` when given, else ``out_dtype``).
     a_row (int32 [M]), if given, gathers row m of A from aq[a_row[m]]."""
     M, K, G, N, A = _gemm_operands(aq, as_, bq, bs, offsets, a_row)
+    if c is not None and c.dtype in (torch.float32, torch.bfloat16):
+        out_dtype = c.dtype                       # a given output buffer sets the type
     c = _out(c, "c", (M, N), out_dtype, aq.device)
     _check("grouped_gemm_fp8_blockscaled", lib.grouped_gemm_fp8_blockscaled(
         _p(aq), _p(as_), _p(a_row), A, _p(bq), _p(bs), _p(offsets), G, M, N, K, _p(c), _dtype_code(c),
@@ -274,3 +282,48 @@ def fp8_block_transpose(q, scale, qt=None, scale_t=None):
     _check("fp8_block_transpose", lib.fp8_block_transpose(_p(q), _p(scale), G, R, C, _p(qt),
                                                           _p(scale_t), _stream()))
     return qt, scale_t
+
+
+def moe_combine_backward(dy, y_perm, dst_row, topk_gate, dq=None, ds=None, d_gate=None):
+    """dy bf16 [T, H], y_perm f32 [T*K, H] -> (dq u8 [T*K, H], ds f32 [T*K, H/128],
+    d_gate f32 [T, K]): the combine's gradient, quantised for the down dgrad."""
+    _need(dy, "dy", torch.bfloat16)
+    _need(y_perm, "y_perm", torch.float32)
+    _need(dst_row, "dst_row", torch.int32)
+    T, K = dst_row.shape
+    H = dy.shape[1]
+    if dy.shape[0] != T or y_perm.shape != (T * K, H):
+        raise ValueError("dy must be [T, H] and y_perm [T*K, H]")
+    _need(topk_gate, "topk_gate", torch.float32, (T, K))
+    dq = _out(dq, "dq", (T * K, H), torch.uint8, dy.device)
+    ds = _out(ds, "ds", (T * K, H // 128), torch.float32, dy.device)
+    d_gate = _out(d_gate, "d_gate", (T, K), torch.float32, dy.device)
+    _check("moe_combine_backward", lib.moe_combine_backward(
+        _p(dy), _p(y_perm), _p(dst_row), _p(topk_gate), T, K, H, _p(dq), _p(ds), _p(d_gate), _stream()))
+    return dq, ds, d_gate
+
+
+def swiglu_backward(gate_up, dh, dq=None, ds=None):
+    """gate_up f32 [M, 2I], dh f32 [M, I] -> (dq u8 [M, 2I], ds f32 [M, 2I/128])."""
+    _need(gate_up, "gate_up", torch.float32)
+    M, twoI = gate_up.shape
+    I = twoI // 2
+    _need(dh, "dh", torch.float32, (M, I))
+    dq = _out(dq, "dq", (M, twoI), torch.uint8, gate_up.device)
+    ds = _out(ds, "ds", (M, twoI // 128), torch.float32, gate_up.device)
+    _check("swiglu_backward", lib.swiglu_backward(_p(gate_up), _p(dh), M, I, _p(dq), _p(ds), _stream()))
+    return dq, ds
+
+
+def moe_route_backward(logits, topk_idx, d_gate, mode="sigmoid_bias", normalize=True, d_logits=None):
+    """-> d_logits f32 [T, E], the router-logit gradient through the selected experts."""
+    _need(logits, "logits", torch.float32)
+    T, E = logits.shape
+    _need(topk_idx, "topk_idx", torch.int32)
+    K = topk_idx.shape[1]
+    _need(d_gate, "d_gate", torch.float32, (T, K))
+    m = ROUTE_SIGMOID_BIAS if mode == "sigmoid_bias" else ROUTE_SOFTMAX_GROUPED
+    d_logits = _out(d_logits, "d_logits", (T, E), torch.float32, logits.device)
+    _check("moe_route_backward", lib.moe_route_backward(
+        _p(logits), _p(topk_idx), _p(d_gate), T, E, K, m, int(bool(normalize)), _p(d_logits), _stream()))
+    return d_logits

@@ -139,3 +139,90 @@ class MoEForward:
         L.moe_combine(b["c2"], b["dst_row"], b["gate"], shared, out=b["y"])
         mark("combine")
         return b["y"]
+
+
+def transpose_weights(w):
+    """Block-transposed FP8 weights for the input-side backward ([KANANA-FP8]:
+    the backward uses the transposed forward weights, not a second
+    quantisation).  Like the weight quantisation, once per optimizer step."""
+    t = {}
+    t["w13tq"], t["w13ts"] = L.fp8_block_transpose(w["w13q"], w["w13s"])   # [E, H, 2I]
+    t["w2tq"], t["w2ts"] = L.fp8_block_transpose(w["w2q"], w["w2s"])       # [E, I, H]
+    if "sw13q" in w:
+        t["sw13tq"], t["sw13ts"] = L.fp8_block_transpose(w["sw13q"], w["sw13s"])
+        t["sw2tq"], t["sw2ts"] = L.fp8_block_transpose(w["sw2q"], w["sw2s"])
+    return t
+
+
+class MoEBackward:
+    """Input-side backward of a MoEForward (dx and the router-logit gradient),
+    enqueued on the current stream (the shared expert's chain on the
+    forward's side stream):
+
+      moe_combine_backward (dC2 quantised, d_gate) -> down dgrad GEMM on W2^T
+      -> swiglu_backward on the forward's gate|up output -> gate|up dgrad GEMM
+      on W13^T -> un-permute sum (moe_combine with unit gates, plus the shared
+      expert's dx) -> moe_route_backward.
+
+    The forward must keep its float32 gate|up output (MoEForward(fused=False)).
+    """
+
+    def __init__(self, fwd, wt):
+        if fwd.fused:
+            raise ValueError("the backward needs the gate|up output: build the forward with fused=False")
+        self.f, self.wt = fwd, wt
+        T, H, E, I, K = fwd.T, fwd.H, fwd.E, fwd.I, fwd.K
+        M = T * K
+        dev = fwd.buf["xq"].device
+        e = lambda shape, dt: torch.empty(shape, dtype=dt, device=dev)
+        self.buf = dict(dc2q=e((M, H), torch.uint8), dc2s=e((M, H // 128), torch.float32),
+                        d_gate=e((T, K), torch.float32), dh=e((M, I), torch.float32),
+                        dq1=e((M, 2 * I), torch.uint8), ds1=e((M, 2 * I // 128), torch.float32),
+                        dxp=e((M, H), torch.float32), ones=torch.ones((T, K), dtype=torch.float32, device=dev),
+                        dx=e((T, H), torch.bfloat16), d_logits=e((T, E), torch.float32))
+        if fwd.shared_I:
+            Is = fwd.shared_I
+            self.buf.update(dyq=e((T, H), torch.uint8), dys=e((T, H // 128), torch.float32),
+                            dhs=e((T, Is), torch.float32), dq1s=e((T, 2 * Is), torch.uint8),
+                            ds1s=e((T, 2 * Is // 128), torch.float32), dxs=e((T, H), torch.float32))
+
+    def __call__(self, dy, logits, on_stage=None):
+        """dy bf16 [T, H], logits f32 [T, E] (the forward's) -> (dx bf16 [T, H],
+        d_logits f32 [T, E])."""
+        mark = on_stage or (lambda name: None)
+        f, fb, b, wt = self.f, self.f.buf, self.buf, self.wt
+        shared = None
+        if f.shared_I:
+            def shared_chain():
+                L.quant_act_1x128_e4m3(dy, q=b["dyq"], scale=b["dys"])
+                L.grouped_gemm_fp8_blockscaled(b["dyq"], b["dys"], wt["sw2tq"], wt["sw2ts"], fb["one_group"],
+                                               c=b["dhs"])
+                L.swiglu_backward(fb["sc1"], b["dhs"], dq=b["dq1s"], ds=b["ds1s"])
+                L.grouped_gemm_fp8_blockscaled(b["dq1s"], b["ds1s"], wt["sw13tq"], wt["sw13ts"], fb["one_group"],
+                                               c=b["dxs"])
+            if f.side is not None:
+                f.side.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(f.side):
+                    shared_chain()
+            else:
+                shared_chain()
+            shared = b["dxs"]
+        L.moe_combine_backward(dy, fb["c2"], fb["dst_row"], fb["gate"], dq=b["dc2q"], ds=b["dc2s"],
+                               d_gate=b["d_gate"])
+        mark("combine_backward")
+        L.grouped_gemm_fp8_blockscaled(b["dc2q"], b["dc2s"], wt["w2tq"], wt["w2ts"], fb["offsets"], c=b["dh"])
+        mark("down_dgrad")
+        L.swiglu_backward(fb["c1"], b["dh"], dq=b["dq1"], ds=b["ds1"])
+        mark("swiglu_backward")
+        L.grouped_gemm_fp8_blockscaled(b["dq1"], b["ds1"], wt["w13tq"], wt["w13ts"], fb["offsets"], c=b["dxp"])
+        mark("gate_up_dgrad")
+        if f.shared_I and f.side is not None:
+            torch.cuda.current_stream().wait_stream(f.side)
+            mark("shared_join")
+        L.moe_combine(b["dxp"], fb["dst_row"], b["ones"], shared, out=b["dx"])
+        mark("unpermute_sum")
+        r = f.route
+        L.moe_route_backward(logits, fb["idx"], b["d_gate"], mode=r["mode"], normalize=r.get("normalize", True),
+                             d_logits=b["d_logits"])
+        mark("route_backward")
+        return b["dx"], b["d_logits"]

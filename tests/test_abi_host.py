@@ -24,7 +24,7 @@ S = None                              # null stream
 
 
 def test_every_declared_symbol_is_exported():
-    assert len(DECLARED) == 12, DECLARED
+    assert len(DECLARED) == 15, DECLARED
     for name in DECLARED:
         assert hasattr(L.lib, name), name
     assert set(DECLARED) == set(L._SIGNATURES)
@@ -133,3 +133,23 @@ def test_binding_requires_device_tensors():
     import torch
     with pytest.raises((ValueError, TypeError)):
         L.quant_act_1x128_e4m3(torch.zeros(4, 128))
+
+
+def test_backward_errors():
+    c = L.lib.moe_combine_backward
+    assert c(P, P, P, P, 4, 2, 100, P, P, P, S) == SHAPE                 # H % 128
+    assert c(P, P, P, P, 4, 17, 128, P, P, P, S) == UNSUP                # K > 16
+    assert c(P, N0, P, P, 4, 2, 128, P, P, P, S) == NULL
+    assert c(PM, P, P, P, 4, 2, 128, P, P, P, S) == ALIGN
+    assert c(N0, N0, N0, N0, 0, 2, 128, N0, N0, N0, S) == OK              # T = 0
+    g = L.lib.swiglu_backward
+    assert g(P, P, 4, 100, P, P, S) == SHAPE
+    assert g(P, N0, 4, 128, P, P, S) == NULL
+    assert g(PM, P, 4, 128, P, P, S) == ALIGN
+    assert g(N0, N0, 0, 128, N0, N0, S) == OK
+    r = L.lib.moe_route_backward
+    assert r(P, P, P, 4, 8, 9, 0, 1, P, S) == SHAPE                       # K > E
+    assert r(P, P, P, 4, 128, 65, 0, 1, P, S) == UNSUP                    # K > 64
+    assert r(P, P, P, 4, 8, 2, 7, 1, P, S) == UNSUP                       # mode
+    assert r(P, P, N0, 4, 8, 2, 0, 1, P, S) == NULL
+    assert r(N0, N0, N0, 0, 8, 2, 1, 0, N0, S) == OK
