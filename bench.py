@@ -7,7 +7,8 @@ quantisation, down GEMM, shared expert, combine) on the DeepSeek-V3-shaped
 workload: T=4096 tokens, hidden 7168, 256 routed experts (top-8 sigmoid with
 bias) + 1 shared expert, SwiGLU inter 2048.  Weights are block-quantised to
 FP8 before the timed region (as in training, once per optimizer step); that
-pass, the backward-side block transpose and the dgrad GEMM are timed
+pass, the backward-side block transpose, the dgrad GEMM, the input-side
+layer backward (with its stages) and the other routing workloads are timed
 separately and reported under "extra".  Inputs are seeded synthetic tensors
 resident in HBM before timing starts.
 
@@ -121,6 +122,18 @@ def extra_rows(cfg, d, fwd, torch, R, synth, reps=5):
     nbytes = dy.numel() * 3 + dys.numel() * 4
     out["quant_act_1x128_dY"] = dict(ms=ms_q, GBps=nbytes / ms_q / 1e6,
                                      frac_hbm=nbytes / ms_q / 1e6 / HBM_PEAK_GBS, bytes=nbytes)
+    # the layer's down projection with bf16 output (same main loop; its bytes
+    # drop by the halved output)
+    bb = fwd.buf
+    c2_bf16 = torch.empty((M, H), dtype=torch.bfloat16, device=wq.device)
+    ms = time_op(lambda: R.grouped_gemm_fp8_blockscaled(bb["hq"], bb["hs"], fwd.w["w2q"], fwd.w["w2s"],
+                                                          bb["offsets"], c=c2_bf16), reps, torch)
+    fl = gemm_flops(M, H, I)
+    nbytes = M * I + M * (I // 128) * 4 + fwd.w["w2q"].numel() + fwd.w["w2s"].numel() * 4 + M * H * 2
+    out["gemm2_down_bf16_out"] = dict(ms=ms, TFLOPs=fl / ms / 1e9, frac_mfma=fl / ms / 1e9 / FP8_PEAK_TFLOPS,
+                                      GBps=nbytes / ms / 1e6, frac_hbm=nbytes / ms / 1e6 / HBM_PEAK_GBS,
+                                      bytes=nbytes, flops=fl)
+    del c2_bf16
     dx = torch.empty((M, H), dtype=torch.float32, device=wq.device)
     offsets = fwd.buf["offsets"]
     ms = time_op(lambda: R.grouped_gemm_fp8_blockscaled(dyq, dys, qt, st, offsets, c=dx), reps, torch)
@@ -129,6 +142,62 @@ def extra_rows(cfg, d, fwd, torch, R, synth, reps=5):
     out["dgrad_grouped_gemm_m32768_n7168_k2048"] = dict(
         ms=ms, TFLOPs=fl / ms / 1e9, frac_mfma=fl / ms / 1e9 / FP8_PEAK_TFLOPS, GBps=nbytes / ms / 1e6,
         frac_hbm=nbytes / ms / 1e6 / HBM_PEAK_GBS, bytes=nbytes, flops=fl)
+    return out
+
+
+def staged(fn, reps, torch):
+    """Mean time of fn(on_stage) and of each stage between its marks, from
+    HIP events recorded on the launching stream."""
+    marks = []
+
+    def on_stage(name):
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        marks[-1].append((name, e))
+
+    fn(None)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        s = torch.cuda.Event(enable_timing=True)
+        s.record()
+        marks.append([("start", s)])
+        fn(on_stage)
+    torch.cuda.synchronize()
+    stages = {}
+    for step in marks:
+        for (_, a), (name, b) in zip(step[:-1], step[1:]):
+            stages[name] = stages.get(name, 0.0) + a.elapsed_time(b) / reps
+    total = sum(step[0][1].elapsed_time(step[-1][1]) for step in marks) / reps
+    return total, stages
+
+
+def backward_rows(cfg, d, w, torch, R, synth, reps=5):
+    """Input-side layer backward on the same workload: the forward that keeps
+    its float32 gate|up output, the block transpose of every expert's
+    weights (once per optimizer step), and the backward chain with its
+    stages (combine backward, down dgrad, SwiGLU backward, gate|up dgrad,
+    un-permute sum, router backward)."""
+    T, H, E, I, K = cfg["T"], cfg["H"], cfg["E"], cfg["I"], cfg["K"]
+    M = T * K
+    dev = d["x"].device
+    ms_t = time_op(lambda: R.transpose_weights(w), 2, torch)
+    wt = R.transpose_weights(w)
+    fwd = R.MoEForward(T, H, E, I, cfg["route"], w, dev, fused=False, shared_I=cfg.get("shared_I"))
+    fwd_ms = time_op(lambda: fwd(d["x"], d["logits"], d["bias"]), reps, torch)
+    dy = synth.output_grad(T, H, dev, seed=4)
+    bwd = R.MoEBackward(fwd, wt)
+    total, st = staged(lambda mark: bwd(dy, d["logits"], on_stage=mark), reps, torch)
+    f_down = gemm_flops(M, I, H)
+    f_gu = gemm_flops(M, H, 2 * I)
+    out = dict(
+        backward_ms=total, tokens_per_s=T / (total / 1e3), forward_keep_c1_ms=fwd_ms,
+        stages_ms=st, transpose_weights_all_ms=ms_t,
+        down_dgrad=dict(ms=st["down_dgrad"], TFLOPs=f_down / st["down_dgrad"] / 1e9,
+                        frac_mfma=f_down / st["down_dgrad"] / 1e9 / FP8_PEAK_TFLOPS),
+        gate_up_dgrad=dict(ms=st["gate_up_dgrad"], TFLOPs=f_gu / st["gate_up_dgrad"] / 1e9,
+                           frac_mfma=f_gu / st["gate_up_dgrad"] / 1e9 / FP8_PEAK_TFLOPS))
+    del bwd, fwd, wt
+    torch.cuda.empty_cache()
     return out
 
 
@@ -323,6 +392,8 @@ def main():
     if not args.no_extra:
         log("extra rows: weight quantisation, block transpose, dgrad")
         extra = extra_rows(cfg, d, fwd, torch, R, synth)
+        log("input-side backward")
+        extra["backward"] = backward_rows(cfg, d, w, torch, R, synth)
         log("other workloads: MoGE and skewed-load layers")
         extra["other_workloads"] = other_workload_rows(torch, R, synth)
     cpu = None
