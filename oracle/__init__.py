@@ -61,6 +61,7 @@ from .combine import combine_ref, combine_fp32_replay
 from .backward import (combine_backward, swiglu_backward, route_backward_sigmoid,
                        route_backward_softmax, layer_backward)
 from .transpose import block_transpose
+from .wgrad import padded_offsets, grouped_rows, quant_act_128x1_grouped, wgrad_gemm, layer_wgrad
 from .layer import layer_forward, layer_forward_dense
 
 __all__ = [
@@ -71,4 +72,5 @@ __all__ = [
     "grouped_gemm_rows", "swiglu_quant", "combine_ref", "combine_fp32_replay",
     "block_transpose", "layer_forward", "layer_forward_dense", "combine_backward",
     "swiglu_backward", "route_backward_sigmoid", "route_backward_softmax", "layer_backward",
+    "padded_offsets", "grouped_rows", "quant_act_128x1_grouped", "wgrad_gemm", "layer_wgrad",
 ]
