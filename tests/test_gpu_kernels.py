@@ -1,7 +1,7 @@
 """Per-kernel parity of the HIP library against the CPU oracle, through the
 C ABI, on seeded inputs that span several tiles, ragged tails and the edge
 cases of each step.  Bit-exact for codes, scales, indices, permutations and
-transposes; GEMMs within 1e-4 of the oracle's magnitude sum; combine
+transposes; GEMMs within 2^-10 of the oracle's magnitude sum; combine
 bit-exact against the documented binary32 order and within 1 bf16 ulp of
 the float64 value."""
 
