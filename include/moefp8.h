@@ -287,6 +287,9 @@ MOE_API moe_status fp8_block_transpose(const uint8_t* q, const float* scale, int
  *            operand of the down projection's dgrad)
  *  d_gate    f32  [T, K] (out): <dy[t], y_perm[dst_row[t,k]]>, summed in a
  *            fixed order (reproducible)
+ *  gate_row  f32  [T*K] (out, optional, NULL to skip): gate_row[dst_row[t,k]]
+ *            = topk_gate[t,k], the gate of each grouped row (the row factor
+ *            of the down projection's weight-gradient operand)
  *  The shared expert's gradient is dy itself (quantise it with
  *  quant_act_1x128_e4m3).  H % 128 == 0, 1 <= K <= 16.
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED (K > 16), MOE_ERR_ALIGN
@@ -294,7 +297,7 @@ MOE_API moe_status fp8_block_transpose(const uint8_t* q, const float* scale, int
  */
 MOE_API moe_status moe_combine_backward(const uint16_t* dy_bf16, const float* y_perm, const int32_t* dst_row,
                                 const float* topk_gate, int32_t T, int32_t K, int32_t H, uint8_t* dq,
-                                float* ds, float* d_gate, void* stream);
+                                float* ds, float* d_gate, float* gate_row, void* stream);
 
 /*
  * swiglu_backward -- gradient of h = silu(g) * u, [g | u] the float32
@@ -305,11 +308,13 @@ MOE_API moe_status moe_combine_backward(const uint16_t* dy_bf16, const float* y_
  *  dq, ds   u8 [M, 2I], f32 [M, 2I/128] (out): [dg | du] quantised in 1x128
  *           tiles, with (binary32, s the sigmoid specification of moe_route):
  *           silu = g*s; dsilu = s*(1 + g*(1 - s)); du = dh*silu; dg = (dh*u)*dsilu
+ *  d        f32 [M, 2I] (out, optional, NULL to skip): [dg | du] unquantised
+ *           (the source of the gate|up weight gradient's 128x1 operand)
  *  I % 128 == 0.
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN (gate_up, dh 16-byte).
  */
 MOE_API moe_status swiglu_backward(const float* gate_up, const float* dh, int64_t M, int32_t I, uint8_t* dq,
-                           float* ds, void* stream);
+                           float* ds, float* d, void* stream);
 
 /*
  * moe_route_backward -- gradient of the gates with respect to the router
@@ -332,6 +337,76 @@ MOE_API moe_status swiglu_backward(const float* gate_up, const float* dh, int64_
 MOE_API moe_status moe_route_backward(const float* logits, const int32_t* topk_idx, const float* d_gate,
                               int32_t T, int32_t E, int32_t K, moe_route_mode mode, int32_t normalize_topk,
                               float* d_logits, void* stream);
+
+/* ------------------------------------------------------------------------
+ * Weight gradients of the expert GEMMs in FP8.  [DSV3-FP8]: most training
+ * GEMMs, backward ones included, run in FP8 with fine-grained scaling.  For
+ * a projection out = in . W_g^T (W_g stored [out, in]) of expert g:
+ *   dW_g[o, i] = sum over the expert's rows r of dOut[r, o] * In[r, i],
+ * a reduction over tokens.  Both operands are quantised in 128x1 tiles
+ * (128 consecutive rows of one expert in one column; each expert's rows are
+ * padded with zero rows to whole tiles so no tile spans two experts; scale
+ * and codes as in the conventions above) and stored transposed, [column,
+ * padded row] with row stride ld, expert g owning the padded rows
+ * [P_g, P_{g+1}), P_g = sum over g' < g of 128 ceil(M_g' / 128).
+ * ------------------------------------------------------------------------ */
+
+/*
+ * moe_wgrad_padded_rows -- host-only: the smallest admissible ld for M
+ * grouped rows in G groups, 128 (ceil(M/128) + G) (an upper bound on P_G).
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE.
+ */
+MOE_API moe_status moe_wgrad_padded_rows(int64_t M, int32_t G, int64_t* rows);
+
+/*
+ * quant_act_128x1_grouped_e4m3 -- 128x1-tile quantisation of a grouped
+ * operand, written transposed.
+ *
+ *  x            [x_rows, C] (f32 or bf16), or with swiglu_input != 0 a float32
+ *               gate|up array [x_rows, 2C] whose rows give h = silu(g) * u
+ *               (the forward's binary32 SwiGLU, g = [:, :C], u = [:, C:])
+ *  row_index    i32 [M] or NULL: grouped row r reads row row_index[r] of x
+ *               (indices clamped into [0, x_rows)); NULL reads row r
+ *  row_scale    f32 [M] or NULL: grouped row r is fl32(row_scale[r] * value)
+ *  group_offsets i32 [G+1] (device): grouped rows of expert g are
+ *               [offsets[g], offsets[g+1]); offsets[G] == M
+ *  ld           row stride of qt (multiple of 128, >= moe_wgrad_padded_rows)
+ *  padded_offsets i32 [G+1] (out): P_0..P_G
+ *  qt           u8  [C, ld] (out): codes; columns [P_g, P_{g+1}) hold expert
+ *               g's rows then zero codes for its padding rows; columns past
+ *               P_G are not written
+ *  st           f32 [C, ld/128] (out): tile scales (tile j of column c at
+ *               st[c, j] for the tiles below P_G)
+ *  C % 128 == 0, 1 <= G <= 1024.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (C, ld, x_rows), MOE_ERR_UNSUPPORTED
+ *         (dtype, G, a bf16 gate|up input), MOE_ERR_ALIGN (x, qt 16-byte).
+ */
+MOE_API moe_status quant_act_128x1_grouped_e4m3(const void* x, moe_dtype x_dtype, int32_t swiglu_input,
+                                        int64_t x_rows, int32_t C, const int32_t* row_index,
+                                        const float* row_scale, const int32_t* group_offsets, int32_t G,
+                                        int64_t M, int64_t ld, int32_t* padded_offsets, uint8_t* qt,
+                                        float* st, void* stream);
+
+/*
+ * grouped_wgrad_fp8 -- dW_g = A_g . B_g^T over expert g's padded rows,
+ * promoted per 128-row chunk:
+ *   dW_g[o, i] = sum_kb P_kb[o, i] * as[o, kb] * bs[i, kb]
+ * with P_kb the FP8 dot product of the chunk (float32 accumulation).
+ *
+ *  aq, as   u8 [Na, ld], f32 [Na, ld/128]   output-gradient operand (dOut^T)
+ *  bq, bs   u8 [Nb, ld], f32 [Nb, ld/128]   input operand (In^T)
+ *  padded_offsets i32 [G+1] (device)   from quant_act_128x1_grouped_e4m3
+ *  c        [G, Na, Nb] (out), f32 or bf16 (RNE): the [out, in] layout of the
+ *           weights; an expert without rows gets zeros.  accumulate != 0
+ *           adds to c's contents instead (c = c + dW in float32, then the
+ *           output type's rounding).
+ *  Na % 128 == Nb % 128 == 0, 1 <= G <= 1024, ld a multiple of 128.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_ALIGN
+ *         (aq, bq 16-byte; c 16-byte for f32, 8-byte for bf16).
+ */
+MOE_API moe_status grouped_wgrad_fp8(const uint8_t* aq, const float* as, const uint8_t* bq, const float* bs,
+                             const int32_t* padded_offsets, int32_t G, int32_t Na, int32_t Nb, int64_t ld,
+                             void* c, moe_dtype c_dtype, int32_t accumulate, void* stream);
 
 #ifdef __cplusplus
 }

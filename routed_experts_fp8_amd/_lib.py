@@ -40,10 +40,17 @@ _SIGNATURES = {
     "fp8_block_transpose": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _i32, _c_void_p, _c_void_p,
                                    _c_void_p]),
     "moe_combine_backward": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
-                                    _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
-    "swiglu_backward": (_i32, [_c_void_p, _c_void_p, _i64, _i32, _c_void_p, _c_void_p, _c_void_p]),
+                                    _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
+    "swiglu_backward": (_i32, [_c_void_p, _c_void_p, _i64, _i32, _c_void_p, _c_void_p, _c_void_p,
+                               _c_void_p]),
     "moe_route_backward": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32,
                                   _c_void_p, _c_void_p]),
+    "moe_wgrad_padded_rows": (_i32, [_i64, _i32, ctypes.POINTER(_i64)]),
+    "quant_act_128x1_grouped_e4m3": (_i32, [_c_void_p, _i32, _i32, _i64, _i32, _c_void_p, _c_void_p,
+                                            _c_void_p, _i32, _i64, _i64, _c_void_p, _c_void_p, _c_void_p,
+                                            _c_void_p]),
+    "grouped_wgrad_fp8": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
+                                 _i64, _c_void_p, _i32, _i32, _c_void_p]),
 }
 
 
@@ -284,9 +291,10 @@ def fp8_block_transpose(q, scale, qt=None, scale_t=None):
     return qt, scale_t
 
 
-def moe_combine_backward(dy, y_perm, dst_row, topk_gate, dq=None, ds=None, d_gate=None):
+def moe_combine_backward(dy, y_perm, dst_row, topk_gate, dq=None, ds=None, d_gate=None, gate_row=None):
     """dy bf16 [T, H], y_perm f32 [T*K, H] -> (dq u8 [T*K, H], ds f32 [T*K, H/128],
-    d_gate f32 [T, K]): the combine's gradient, quantised for the down dgrad."""
+    d_gate f32 [T, K]): the combine's gradient, quantised for the down dgrad.
+    gate_row (f32 [T*K], optional) receives each grouped row's gate."""
     _need(dy, "dy", torch.bfloat16)
     _need(y_perm, "y_perm", torch.float32)
     _need(dst_row, "dst_row", torch.int32)
@@ -298,20 +306,26 @@ def moe_combine_backward(dy, y_perm, dst_row, topk_gate, dq=None, ds=None, d_gat
     dq = _out(dq, "dq", (T * K, H), torch.uint8, dy.device)
     ds = _out(ds, "ds", (T * K, H // 128), torch.float32, dy.device)
     d_gate = _out(d_gate, "d_gate", (T, K), torch.float32, dy.device)
+    if gate_row is not None:
+        _need(gate_row, "gate_row", torch.float32, (T * K,))
     _check("moe_combine_backward", lib.moe_combine_backward(
-        _p(dy), _p(y_perm), _p(dst_row), _p(topk_gate), T, K, H, _p(dq), _p(ds), _p(d_gate), _stream()))
+        _p(dy), _p(y_perm), _p(dst_row), _p(topk_gate), T, K, H, _p(dq), _p(ds), _p(d_gate), _p(gate_row),
+        _stream()))
     return dq, ds, d_gate
 
 
-def swiglu_backward(gate_up, dh, dq=None, ds=None):
-    """gate_up f32 [M, 2I], dh f32 [M, I] -> (dq u8 [M, 2I], ds f32 [M, 2I/128])."""
+def swiglu_backward(gate_up, dh, dq=None, ds=None, d=None):
+    """gate_up f32 [M, 2I], dh f32 [M, I] -> (dq u8 [M, 2I], ds f32 [M, 2I/128]).
+    d (f32 [M, 2I], optional) receives [dg | du] unquantised."""
     _need(gate_up, "gate_up", torch.float32)
     M, twoI = gate_up.shape
     I = twoI // 2
     _need(dh, "dh", torch.float32, (M, I))
     dq = _out(dq, "dq", (M, twoI), torch.uint8, gate_up.device)
     ds = _out(ds, "ds", (M, twoI // 128), torch.float32, gate_up.device)
-    _check("swiglu_backward", lib.swiglu_backward(_p(gate_up), _p(dh), M, I, _p(dq), _p(ds), _stream()))
+    if d is not None:
+        _need(d, "d", torch.float32, (M, twoI))
+    _check("swiglu_backward", lib.swiglu_backward(_p(gate_up), _p(dh), M, I, _p(dq), _p(ds), _p(d), _stream()))
     return dq, ds
 
 
@@ -327,3 +341,60 @@ def moe_route_backward(logits, topk_idx, d_gate, mode="sigmoid_bias", normalize=
     _check("moe_route_backward", lib.moe_route_backward(
         _p(logits), _p(topk_idx), _p(d_gate), T, E, K, m, int(bool(normalize)), _p(d_logits), _stream()))
     return d_logits
+
+
+def moe_wgrad_padded_rows(M, G):
+    """Smallest admissible row stride of the 128x1-quantised operands."""
+    n = _i64(0)
+    _check("moe_wgrad_padded_rows", lib.moe_wgrad_padded_rows(int(M), int(G), ctypes.byref(n)))
+    return n.value
+
+
+def quant_act_128x1_grouped_e4m3(x, group_offsets, M=None, row_index=None, row_scale=None, swiglu_input=False,
+                                 ld=None, qt=None, st=None, padded_offsets=None):
+    """128x1 (token-dimension) quantisation of a grouped operand, transposed:
+    x [x_rows, C] (f32/bf16) or, with swiglu_input, f32 gate|up [x_rows, 2C]
+    -> (qt u8 [C, ld], st f32 [C, ld/128], padded_offsets i32 [G+1])."""
+    if x.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("x must be float32 or bfloat16")
+    _need(x, "x", x.dtype)
+    x_rows, cols = x.shape
+    C = cols // 2 if swiglu_input else cols
+    _need(group_offsets, "group_offsets", torch.int32)
+    G = group_offsets.shape[0] - 1
+    if M is None:
+        M = row_index.shape[0] if row_index is not None else x_rows
+    if row_index is not None:
+        _need(row_index, "row_index", torch.int32, (M,))
+    if row_scale is not None:
+        _need(row_scale, "row_scale", torch.float32, (M,))
+    ld = moe_wgrad_padded_rows(M, G) if ld is None else int(ld)
+    qt = _out(qt, "qt", (C, ld), torch.uint8, x.device)
+    st = _out(st, "st", (C, ld // 128), torch.float32, x.device)
+    padded_offsets = _out(padded_offsets, "padded_offsets", (G + 1,), torch.int32, x.device)
+    _check("quant_act_128x1_grouped_e4m3", lib.quant_act_128x1_grouped_e4m3(
+        _p(x), _dtype_code(x), int(bool(swiglu_input)), x_rows, C, _p(row_index), _p(row_scale),
+        _p(group_offsets), G, M, ld, _p(padded_offsets), _p(qt), _p(st), _stream()))
+    return qt, st, padded_offsets
+
+
+def grouped_wgrad_fp8(aq, as_, bq, bs, padded_offsets, out_dtype=torch.float32, c=None, accumulate=False):
+    """dW [G, Na, Nb] = per-expert dOut^T . In over the 128x1-quantised operands
+    aq [Na, ld] (output gradient) and bq [Nb, ld] (input)."""
+    _need(aq, "aq", torch.uint8)
+    Na, ld = aq.shape
+    _need(as_, "as", torch.float32, (Na, ld // 128))
+    _need(bq, "bq", torch.uint8)
+    Nb = bq.shape[0]
+    if bq.shape[1] != ld:
+        raise ValueError("aq and bq must share the padded row stride")
+    _need(bs, "bs", torch.float32, (Nb, ld // 128))
+    _need(padded_offsets, "padded_offsets", torch.int32)
+    G = padded_offsets.shape[0] - 1
+    if c is not None and c.dtype in (torch.float32, torch.bfloat16):
+        out_dtype = c.dtype
+    c = _out(c, "c", (G, Na, Nb), out_dtype, aq.device)
+    _check("grouped_wgrad_fp8", lib.grouped_wgrad_fp8(
+        _p(aq), _p(as_), _p(bq), _p(bs), _p(padded_offsets), G, Na, Nb, ld, _p(c), _dtype_code(c),
+        int(bool(accumulate)), _stream()))
+    return c

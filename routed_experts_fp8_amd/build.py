@@ -27,7 +27,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["status.cpp", "quant.hip", "transpose.hip", "route.hip", "permute.hip",
-           "swiglu_combine.hip", "gemm.hip", "backward.hip"]
+           "swiglu_combine.hip", "gemm.hip", "backward.hip", "wgrad.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

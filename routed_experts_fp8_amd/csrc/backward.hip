@@ -41,9 +41,15 @@ constexpr int kMaxK = 16;  // slots per token held in registers by the combine b
 __global__ __launch_bounds__(256) void combine_backward_kernel(
     const uint16_t* __restrict__ dy, const float* __restrict__ y_perm, const int* __restrict__ dst_row,
     const float* __restrict__ gate, int K, int H, uint8_t* __restrict__ dq, float* __restrict__ ds,
-    float* __restrict__ d_gate) {
+    float* __restrict__ d_gate, float* __restrict__ gate_row) {
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x;
+  const int64_t n_rows = (int64_t)gridDim.x * K;  // T * K grouped rows
+  auto row_of = [&](int k) {                        // dst_row clamped into range
+    const int64_t r = dst_row[t * K + k];
+    return r < 0 ? (int64_t)0 : (r >= n_rows ? n_rows - 1 : r);
+  };
+  if (gate_row && tid < K) gate_row[row_of(tid)] = gate[t * K + tid];
   float part[kMaxK];
 #pragma unroll
   for (int k = 0; k < kMaxK; ++k) part[k] = 0.f;
@@ -64,7 +70,7 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
 #pragma unroll
     for (int k = 0; k < kMaxK; ++k) {
       if (k < K) {  // uniform
-        const int64_t r = dst_row[t * K + k];
+        const int64_t r = row_of(k);
         const float g = gate[t * K + k];
         float p[8];
         float amax = 0.f;
@@ -110,7 +116,8 @@ __global__ __launch_bounds__(256) void combine_backward_kernel(
 __global__ __launch_bounds__(256) void swiglu_backward_kernel(const float* __restrict__ gu,
                                                               const float* __restrict__ dh, int64_t M,
                                                               int I, uint8_t* __restrict__ dq,
-                                                              float* __restrict__ ds) {
+                                                              float* __restrict__ ds,
+                                                              float* __restrict__ d_out) {
   const int64_t nvec = M * (int64_t)(I / 4);  // 4 values of dh per lane
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   const int qv = I / 4;
@@ -153,6 +160,10 @@ __global__ __launch_bounds__(256) void swiglu_backward_kernel(const float* __res
       if ((c4 & 31) == 0) {
         ds[m * nb + c4 / 32] = sg;
         ds[m * nb + I / 128 + c4 / 32] = su;
+      }
+      if (d_out) {
+        *reinterpret_cast<float4*>(d_out + m * 2 * I + 4 * c4) = make_float4(dg[0], dg[1], dg[2], dg[3]);
+        *reinterpret_cast<float4*>(d_out + m * 2 * I + I + 4 * c4) = make_float4(du[0], du[1], du[2], du[3]);
       }
     }
   }
@@ -221,7 +232,8 @@ using namespace moefp8;
 
 extern "C" moe_status moe_combine_backward(const uint16_t* dy_bf16, const float* y_perm, const int32_t* dst_row,
                                            const float* topk_gate, int32_t T, int32_t K, int32_t H,
-                                           uint8_t* dq, float* ds, float* d_gate, void* stream) {
+                                           uint8_t* dq, float* ds, float* d_gate, float* gate_row,
+                                           void* stream) {
   clear_detail();
   MOE_REQUIRE(T >= 0 && K >= 1 && H > 0 && H % 128 == 0, MOE_ERR_SHAPE,
               "T=%d K=%d H=%d (H a positive multiple of 128)", T, K, H);
@@ -230,27 +242,27 @@ extern "C" moe_status moe_combine_backward(const uint16_t* dy_bf16, const float*
   MOE_REQUIRE(dy_bf16 && y_perm && dst_row && topk_gate && dq && ds && d_gate, MOE_ERR_NULL,
               "every array is required");
   MOE_REQUIRE(aligned(dy_bf16, 16) && aligned(y_perm, 16) && aligned(dq, 8) && aligned(ds, 4) &&
-                  aligned(dst_row, 4) && aligned(topk_gate, 4) && aligned(d_gate, 4),
+                  aligned(dst_row, 4) && aligned(topk_gate, 4) && aligned(d_gate, 4) && aligned(gate_row, 4),
               MOE_ERR_ALIGN, "dy and y_perm need 16-byte alignment, dq 8-byte");
   hipStream_t st = as_stream(stream);
   combine_backward_kernel<<<(unsigned)T, 256, 0, st>>>(dy_bf16, y_perm, dst_row, topk_gate, K, H, dq, ds,
-                                                       d_gate);
+                                                       d_gate, gate_row);
   return after_launch("moe_combine_backward", st);
 }
 
 extern "C" moe_status swiglu_backward(const float* gate_up, const float* dh, int64_t M, int32_t I, uint8_t* dq,
-                                      float* ds, void* stream) {
+                                      float* ds, float* d, void* stream) {
   clear_detail();
   MOE_REQUIRE(M >= 0 && I > 0 && I % 128 == 0, MOE_ERR_SHAPE, "M=%lld I=%d (I a positive multiple of 128)",
               (long long)M, I);
   if (M == 0) return MOE_OK;
   MOE_REQUIRE(gate_up && dh && dq && ds, MOE_ERR_NULL, "gate_up, dh, dq and ds are required");
-  MOE_REQUIRE(aligned(gate_up, 16) && aligned(dh, 16) && aligned(dq, 4) && aligned(ds, 4), MOE_ERR_ALIGN,
-              "gate_up and dh need 16-byte alignment");
+  MOE_REQUIRE(aligned(gate_up, 16) && aligned(dh, 16) && aligned(dq, 4) && aligned(ds, 4) && aligned(d, 16),
+              MOE_ERR_ALIGN, "gate_up, dh and d need 16-byte alignment");
   hipStream_t st = as_stream(stream);
   const int64_t nvec = M * (I / 4);
   const int64_t need = (nvec + 255) / 256;
-  swiglu_backward_kernel<<<(unsigned)(need < 16384 ? need : 16384), 256, 0, st>>>(gate_up, dh, M, I, dq, ds);
+  swiglu_backward_kernel<<<(unsigned)(need < 16384 ? need : 16384), 256, 0, st>>>(gate_up, dh, M, I, dq, ds, d);
   return after_launch("swiglu_backward", st);
 }
 

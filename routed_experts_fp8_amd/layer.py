@@ -165,9 +165,12 @@ class MoEBackward:
       expert's dx) -> moe_route_backward.
 
     The forward must keep its float32 gate|up output (MoEForward(fused=False)).
+    With ``weight_grad=True`` the backward also keeps what the weight
+    gradients need (each grouped row's gate and the unquantised [dg | du]);
+    ``MoEWeightGrad`` consumes them.
     """
 
-    def __init__(self, fwd, wt):
+    def __init__(self, fwd, wt, weight_grad=False):
         if fwd.fused:
             raise ValueError("the backward needs the gate|up output: build the forward with fused=False")
         self.f, self.wt = fwd, wt
@@ -180,6 +183,11 @@ class MoEBackward:
                         dq1=e((M, 2 * I), torch.uint8), ds1=e((M, 2 * I // 128), torch.float32),
                         dxp=e((M, H), torch.float32), ones=torch.ones((T, K), dtype=torch.float32, device=dev),
                         dx=e((T, H), torch.bfloat16), d_logits=e((T, E), torch.float32))
+        self.weight_grad = weight_grad
+        if weight_grad:
+            self.buf.update(gate_row=e((M,), torch.float32), d1=e((M, 2 * I), torch.float32))
+            if fwd.shared_I:
+                self.buf["d1s"] = e((T, 2 * fwd.shared_I), torch.float32)
         if fwd.shared_I:
             Is = fwd.shared_I
             self.buf.update(dyq=e((T, H), torch.uint8), dys=e((T, H // 128), torch.float32),
@@ -197,7 +205,7 @@ class MoEBackward:
                 L.quant_act_1x128_e4m3(dy, q=b["dyq"], scale=b["dys"])
                 L.grouped_gemm_fp8_blockscaled(b["dyq"], b["dys"], wt["sw2tq"], wt["sw2ts"], fb["one_group"],
                                                c=b["dhs"])
-                L.swiglu_backward(fb["sc1"], b["dhs"], dq=b["dq1s"], ds=b["ds1s"])
+                L.swiglu_backward(fb["sc1"], b["dhs"], dq=b["dq1s"], ds=b["ds1s"], d=b.get("d1s"))
                 L.grouped_gemm_fp8_blockscaled(b["dq1s"], b["ds1s"], wt["sw13tq"], wt["sw13ts"], fb["one_group"],
                                                c=b["dxs"])
             if f.side is not None:
@@ -208,11 +216,11 @@ class MoEBackward:
                 shared_chain()
             shared = b["dxs"]
         L.moe_combine_backward(dy, fb["c2"], fb["dst_row"], fb["gate"], dq=b["dc2q"], ds=b["dc2s"],
-                               d_gate=b["d_gate"])
+                               d_gate=b["d_gate"], gate_row=b.get("gate_row"))
         mark("combine_backward")
         L.grouped_gemm_fp8_blockscaled(b["dc2q"], b["dc2s"], wt["w2tq"], wt["w2ts"], fb["offsets"], c=b["dh"])
         mark("down_dgrad")
-        L.swiglu_backward(fb["c1"], b["dh"], dq=b["dq1"], ds=b["ds1"])
+        L.swiglu_backward(fb["c1"], b["dh"], dq=b["dq1"], ds=b["ds1"], d=b.get("d1"))
         mark("swiglu_backward")
         L.grouped_gemm_fp8_blockscaled(b["dq1"], b["ds1"], wt["w13tq"], wt["w13ts"], fb["offsets"], c=b["dxp"])
         mark("gate_up_dgrad")
@@ -226,3 +234,86 @@ class MoEBackward:
                              d_logits=b["d_logits"])
         mark("route_backward")
         return b["dx"], b["d_logits"]
+
+
+class MoEWeightGrad:
+    """FP8 weight gradients of the expert projections after a MoEBackward
+    built with ``weight_grad=True`` ([DSV3-FP8]: backward GEMMs in FP8).
+
+    For each projection out = in . W^T the two operands are re-quantised in
+    128x1 tiles along the token dimension, per expert (zero-padded to whole
+    tiles), stored transposed, and multiplied per expert:
+      down:    dOut = gate * dy (grouped rows; dy gathered through src_token,
+               times each row's gate), In = h = silu(g) * u of the forward's
+               gate|up output                      -> dw2  [E, H, I]
+      gate|up: dOut = [dg | du] of the SwiGLU backward, In = x (gathered)
+                                                   -> dw13 [E, 2I, H]
+    and the same for the shared expert (one group over all tokens; dOut of
+    its down projection is dy itself).  ``__call__(x, dy)`` enqueues
+    everything on the current stream and returns the gradient dict;
+    ``accumulate=True`` adds into the previous call's gradients.
+    """
+
+    def __init__(self, bwd, out_dtype=torch.float32):
+        if not bwd.weight_grad:
+            raise ValueError("build the MoEBackward with weight_grad=True")
+        f = bwd.f
+        self.b, self.f = bwd, f
+        T, H, E, I, K = f.T, f.H, f.E, f.I, f.K
+        M = T * K
+        dev = f.buf["xq"].device
+        e = lambda shape, dt: torch.empty(shape, dtype=dt, device=dev)
+        ld = L.moe_wgrad_padded_rows(M, E)
+        self.ld = ld
+        self.buf = dict(poff=e((E + 1,), torch.int32),
+                        dc2t=e((H, ld), torch.uint8), dc2ts=e((H, ld // 128), torch.float32),
+                        ht=e((I, ld), torch.uint8), hts=e((I, ld // 128), torch.float32),
+                        d1t=e((2 * I, ld), torch.uint8), d1ts=e((2 * I, ld // 128), torch.float32),
+                        xt=e((H, ld), torch.uint8), xts=e((H, ld // 128), torch.float32),
+                        dw2=e((E, H, I), out_dtype), dw13=e((E, 2 * I, H), out_dtype))
+        if f.shared_I:
+            Is = f.shared_I
+            lds = L.moe_wgrad_padded_rows(T, 1)
+            self.lds = lds
+            self.buf.update(spoff=e((2,), torch.int32),
+                            sdyt=e((H, lds), torch.uint8), sdyts=e((H, lds // 128), torch.float32),
+                            sht=e((Is, lds), torch.uint8), shts=e((Is, lds // 128), torch.float32),
+                            sd1t=e((2 * Is, lds), torch.uint8), sd1ts=e((2 * Is, lds // 128), torch.float32),
+                            sxt=e((H, lds), torch.uint8), sxts=e((H, lds // 128), torch.float32),
+                            sdw2=e((1, H, Is), out_dtype), sdw13=e((1, 2 * Is, H), out_dtype))
+
+    def __call__(self, x, dy, accumulate=False, on_stage=None):
+        mark = on_stage or (lambda name: None)
+        f, fb, bb, b = self.f, self.f.buf, self.b.buf, self.buf
+        off, src, ld = fb["offsets"], fb["src_token"], self.ld
+        M = src.shape[0]
+        L.quant_act_128x1_grouped_e4m3(dy, off, M=M, row_index=src, row_scale=bb["gate_row"], ld=ld,
+                                       qt=b["dc2t"], st=b["dc2ts"], padded_offsets=b["poff"])
+        L.quant_act_128x1_grouped_e4m3(fb["c1"], off, swiglu_input=True, ld=ld, qt=b["ht"], st=b["hts"],
+                                       padded_offsets=b["poff"])
+        mark("quant_down_operands")
+        L.grouped_wgrad_fp8(b["dc2t"], b["dc2ts"], b["ht"], b["hts"], b["poff"], c=b["dw2"], accumulate=accumulate)
+        mark("down_wgrad")
+        L.quant_act_128x1_grouped_e4m3(bb["d1"], off, ld=ld, qt=b["d1t"], st=b["d1ts"], padded_offsets=b["poff"])
+        L.quant_act_128x1_grouped_e4m3(x, off, M=M, row_index=src, ld=ld, qt=b["xt"], st=b["xts"],
+                                       padded_offsets=b["poff"])
+        mark("quant_gate_up_operands")
+        L.grouped_wgrad_fp8(b["d1t"], b["d1ts"], b["xt"], b["xts"], b["poff"], c=b["dw13"],
+                            accumulate=accumulate)
+        mark("gate_up_wgrad")
+        out = dict(dw2=b["dw2"], dw13=b["dw13"])
+        if f.shared_I:
+            one, lds = fb["one_group"], self.lds
+            L.quant_act_128x1_grouped_e4m3(dy, one, ld=lds, qt=b["sdyt"], st=b["sdyts"], padded_offsets=b["spoff"])
+            L.quant_act_128x1_grouped_e4m3(fb["sc1"], one, swiglu_input=True, ld=lds, qt=b["sht"], st=b["shts"],
+                                           padded_offsets=b["spoff"])
+            L.grouped_wgrad_fp8(b["sdyt"], b["sdyts"], b["sht"], b["shts"], b["spoff"], c=b["sdw2"],
+                                accumulate=accumulate)
+            L.quant_act_128x1_grouped_e4m3(bb["d1s"], one, ld=lds, qt=b["sd1t"], st=b["sd1ts"],
+                                           padded_offsets=b["spoff"])
+            L.quant_act_128x1_grouped_e4m3(x, one, ld=lds, qt=b["sxt"], st=b["sxts"], padded_offsets=b["spoff"])
+            L.grouped_wgrad_fp8(b["sd1t"], b["sd1ts"], b["sxt"], b["sxts"], b["spoff"], c=b["sdw13"],
+                                accumulate=accumulate)
+            mark("shared_wgrad")
+            out.update(shared_dw2=b["sdw2"], shared_dw13=b["sdw13"])
+        return out

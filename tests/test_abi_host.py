@@ -24,7 +24,7 @@ S = None                              # null stream
 
 
 def test_every_declared_symbol_is_exported():
-    assert len(DECLARED) == 15, DECLARED
+    assert len(DECLARED) == 18, DECLARED
     for name in DECLARED:
         assert hasattr(L.lib, name), name
     assert set(DECLARED) == set(L._SIGNATURES)
@@ -137,19 +137,55 @@ def test_binding_requires_device_tensors():
 
 def test_backward_errors():
     c = L.lib.moe_combine_backward
-    assert c(P, P, P, P, 4, 2, 100, P, P, P, S) == SHAPE                 # H % 128
-    assert c(P, P, P, P, 4, 17, 128, P, P, P, S) == UNSUP                # K > 16
-    assert c(P, N0, P, P, 4, 2, 128, P, P, P, S) == NULL
-    assert c(PM, P, P, P, 4, 2, 128, P, P, P, S) == ALIGN
-    assert c(N0, N0, N0, N0, 0, 2, 128, N0, N0, N0, S) == OK              # T = 0
+    assert c(P, P, P, P, 4, 2, 100, P, P, P, N0, S) == SHAPE             # H % 128
+    assert c(P, P, P, P, 4, 17, 128, P, P, P, N0, S) == UNSUP            # K > 16
+    assert c(P, N0, P, P, 4, 2, 128, P, P, P, N0, S) == NULL
+    assert c(PM, P, P, P, 4, 2, 128, P, P, P, N0, S) == ALIGN
+    assert c(P, P, P, P, 4, 2, 128, P, P, P, ctypes.c_void_p(0x10002), S) == ALIGN   # gate_row
+    assert c(N0, N0, N0, N0, 0, 2, 128, N0, N0, N0, N0, S) == OK          # T = 0
     g = L.lib.swiglu_backward
-    assert g(P, P, 4, 100, P, P, S) == SHAPE
-    assert g(P, N0, 4, 128, P, P, S) == NULL
-    assert g(PM, P, 4, 128, P, P, S) == ALIGN
-    assert g(N0, N0, 0, 128, N0, N0, S) == OK
+    assert g(P, P, 4, 100, P, P, N0, S) == SHAPE
+    assert g(P, N0, 4, 128, P, P, N0, S) == NULL
+    assert g(PM, P, 4, 128, P, P, N0, S) == ALIGN
+    assert g(P, P, 4, 128, P, P, PM, S) == ALIGN                          # d needs 16 bytes
+    assert g(N0, N0, 0, 128, N0, N0, N0, S) == OK
     r = L.lib.moe_route_backward
     assert r(P, P, P, 4, 8, 9, 0, 1, P, S) == SHAPE                       # K > E
     assert r(P, P, P, 4, 128, 65, 0, 1, P, S) == UNSUP                    # K > 64
     assert r(P, P, P, 4, 8, 2, 7, 1, P, S) == UNSUP                       # mode
     assert r(P, P, N0, 4, 8, 2, 0, 1, P, S) == NULL
     assert r(N0, N0, N0, 0, 8, 2, 1, 0, N0, S) == OK
+
+
+def test_wgrad_errors():
+    n = ctypes.c_int64(0)
+    assert L.lib.moe_wgrad_padded_rows(300, 4, ctypes.byref(n)) == OK and n.value == 128 * (3 + 4)
+    assert L.lib.moe_wgrad_padded_rows(0, 1, ctypes.byref(n)) == OK and n.value == 128
+    assert L.lib.moe_wgrad_padded_rows(-1, 1, ctypes.byref(n)) == SHAPE
+    assert L.lib.moe_wgrad_padded_rows(5, 0, ctypes.byref(n)) == SHAPE
+    assert L.lib.moe_wgrad_padded_rows(5, 1, None) == NULL
+    q = L.lib.quant_act_128x1_grouped_e4m3
+    #     x  dt sw rows  C   idx scl off  G   M   ld    poff qt st
+    assert q(P, 0, 0, 300, 100, N0, N0, P, 4, 300, 896, P, P, P, S) == SHAPE       # C % 128
+    assert q(P, 0, 0, 300, 128, N0, N0, P, 4, 300, 768, P, P, P, S) == SHAPE       # ld < 128 (3 + 4)
+    assert "ld" in _detail()
+    assert q(P, 0, 0, 300, 128, N0, N0, P, 4, 300, 900, P, P, P, S) == SHAPE       # ld % 128
+    assert q(P, 0, 0, 200, 128, N0, N0, P, 4, 300, 896, P, P, P, S) == SHAPE       # x_rows < M, no index
+    assert q(P, 1, 1, 300, 128, N0, N0, P, 4, 300, 896, P, P, P, S) == UNSUP       # bf16 gate|up
+    assert q(P, 5, 0, 300, 128, N0, N0, P, 4, 300, 896, P, P, P, S) == UNSUP       # dtype
+    assert q(P, 0, 0, 300, 128, N0, N0, P, 1025, 300, 128 * 1028, P, P, P, S) == UNSUP   # G
+    assert q(P, 0, 0, 300, 128, N0, N0, P, 0, 300, 896, P, P, P, S) == UNSUP       # G = 0
+    assert q(P, 0, 0, 300, 128, N0, N0, N0, 4, 300, 896, P, P, P, S) == NULL      # offsets
+    assert q(N0, 0, 0, 300, 128, N0, N0, P, 4, 300, 896, P, P, P, S) == NULL      # x
+    assert q(PM, 0, 0, 300, 128, N0, N0, P, 4, 300, 896, P, P, P, S) == ALIGN
+    assert q(P, 0, 0, 300, 128, N0, N0, P, 4, 300, 896, P, PM, P, S) == ALIGN     # qt
+    w = L.lib.grouped_wgrad_fp8
+    #     aq as bq bs poff G  Na   Nb   ld   c dt acc
+    assert w(P, P, P, P, P, 4, 100, 128, 256, P, 0, 0, S) == SHAPE
+    assert w(P, P, P, P, P, 4, 128, 128, 200, P, 0, 0, S) == SHAPE                 # ld % 128
+    assert w(P, P, P, P, P, 0, 128, 128, 256, P, 0, 0, S) == UNSUP
+    assert w(P, P, P, P, P, 4, 128, 128, 256, P, 3, 0, S) == UNSUP                 # c dtype
+    assert w(P, P, P, P, N0, 4, 128, 128, 256, P, 0, 0, S) == NULL
+    assert w(P, P, PM, P, P, 4, 128, 128, 256, P, 0, 0, S) == ALIGN
+    assert w(P, P, P, P, P, 4, 128, 128, 256, ctypes.c_void_p(0x10008), 0, 0, S) == ALIGN   # f32 c
+    assert w(P, P, P, P, P, 1024, 262144, 262144, 256, P, 0, 0, S) == UNSUP        # tile count
