@@ -196,7 +196,30 @@ def backward_rows(cfg, d, w, torch, R, synth, reps=5):
                         frac_mfma=f_down / st["down_dgrad"] / 1e9 / FP8_PEAK_TFLOPS),
         gate_up_dgrad=dict(ms=st["gate_up_dgrad"], TFLOPs=f_gu / st["gate_up_dgrad"] / 1e9,
                            frac_mfma=f_gu / st["gate_up_dgrad"] / 1e9 / FP8_PEAK_TFLOPS))
-    del bwd, fwd, wt
+    # weight gradients (128x1 operands + grouped wgrad GEMMs), float32 out
+    bwd = R.MoEBackward(fwd, wt, weight_grad=True)
+    bwd(dy, d["logits"])
+    wg = R.MoEWeightGrad(bwd)
+    total_w, st_w = staged(lambda mark: wg(d["x"], dy, on_stage=mark), reps, torch)
+    ld = wg.ld
+    b2 = 4 * E * H * I + (H + I) * ld + 4 * (H + I) * (ld // 128)
+    b13 = 4 * E * 2 * I * H + (2 * I + H) * ld + 4 * (2 * I + H) * (ld // 128)
+    rows = {}
+    for name, stage, nbytes, fl in (("down_wgrad", "down_wgrad", b2, gemm_flops(M, H, I)),
+                                    ("gate_up_wgrad", "gate_up_wgrad", b13, gemm_flops(M, 2 * I, H))):
+        ms = st_w[stage]
+        rows[name] = dict(ms=ms, GBps=nbytes / ms / 1e6, frac_hbm=nbytes / ms / 1e6 / HBM_PEAK_GBS, bytes=nbytes,
+                          TFLOPs=fl / ms / 1e9, frac_mfma=fl / ms / 1e9 / FP8_PEAK_TFLOPS)
+    # the same gate|up weight gradient with bf16 output
+    wb = wg.buf
+    dwb = torch.empty((E, 2 * I, H), dtype=torch.bfloat16, device=dev)
+    ms = time_op(lambda: R.grouped_wgrad_fp8(wb["d1t"], wb["d1ts"], wb["xt"], wb["xts"], wb["poff"], c=dwb),
+                 reps, torch)
+    nb = b13 - 2 * E * 2 * I * H
+    rows["gate_up_wgrad_bf16_out"] = dict(ms=ms, GBps=nb / ms / 1e6, frac_hbm=nb / ms / 1e6 / HBM_PEAK_GBS,
+                                          bytes=nb)
+    out["weight_grad"] = dict(ms=total_w, stages_ms=st_w, padded_rows=ld, **rows)
+    del bwd, wg, dwb, fwd, wt
     torch.cuda.empty_cache()
     return out
 

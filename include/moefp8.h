@@ -375,8 +375,8 @@ MOE_API moe_status moe_wgrad_padded_rows(int64_t M, int32_t G, int64_t* rows);
  *  qt           u8  [C, ld] (out): codes; columns [P_g, P_{g+1}) hold expert
  *               g's rows then zero codes for its padding rows; columns past
  *               P_G are not written
- *  st           f32 [C, ld/128] (out): tile scales (tile j of column c at
- *               st[c, j] for the tiles below P_G)
+ *  st           f32 [ld/128, C] (out): tile scales, tile-major (tile j of
+ *               column c at st[j, c], for the tiles below P_G)
  *  C % 128 == 0, 1 <= G <= 1024.
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (C, ld, x_rows), MOE_ERR_UNSUPPORTED
  *         (dtype, G, a bf16 gate|up input), MOE_ERR_ALIGN (x, qt 16-byte).
@@ -390,11 +390,11 @@ MOE_API moe_status quant_act_128x1_grouped_e4m3(const void* x, moe_dtype x_dtype
 /*
  * grouped_wgrad_fp8 -- dW_g = A_g . B_g^T over expert g's padded rows,
  * promoted per 128-row chunk:
- *   dW_g[o, i] = sum_kb P_kb[o, i] * as[o, kb] * bs[i, kb]
+ *   dW_g[o, i] = sum_kb P_kb[o, i] * as[kb, o] * bs[kb, i]
  * with P_kb the FP8 dot product of the chunk (float32 accumulation).
  *
- *  aq, as   u8 [Na, ld], f32 [Na, ld/128]   output-gradient operand (dOut^T)
- *  bq, bs   u8 [Nb, ld], f32 [Nb, ld/128]   input operand (In^T)
+ *  aq, as   u8 [Na, ld], f32 [ld/128, Na]   output-gradient operand (dOut^T)
+ *  bq, bs   u8 [Nb, ld], f32 [ld/128, Nb]   input operand (In^T)
  *  padded_offsets i32 [G+1] (device)   from quant_act_128x1_grouped_e4m3
  *  c        [G, Na, Nb] (out), f32 or bf16 (RNE): the [out, in] layout of the
  *           weights; an expert without rows gets zeros.  accumulate != 0

@@ -354,7 +354,7 @@ def quant_act_128x1_grouped_e4m3(x, group_offsets, M=None, row_index=None, row_s
                                  ld=None, qt=None, st=None, padded_offsets=None):
     """128x1 (token-dimension) quantisation of a grouped operand, transposed:
     x [x_rows, C] (f32/bf16) or, with swiglu_input, f32 gate|up [x_rows, 2C]
-    -> (qt u8 [C, ld], st f32 [C, ld/128], padded_offsets i32 [G+1])."""
+    -> (qt u8 [C, ld], st f32 [ld/128, C] (tile-major), padded_offsets i32 [G+1])."""
     if x.dtype not in (torch.float32, torch.bfloat16):
         raise TypeError("x must be float32 or bfloat16")
     _need(x, "x", x.dtype)
@@ -370,7 +370,7 @@ def quant_act_128x1_grouped_e4m3(x, group_offsets, M=None, row_index=None, row_s
         _need(row_scale, "row_scale", torch.float32, (M,))
     ld = moe_wgrad_padded_rows(M, G) if ld is None else int(ld)
     qt = _out(qt, "qt", (C, ld), torch.uint8, x.device)
-    st = _out(st, "st", (C, ld // 128), torch.float32, x.device)
+    st = _out(st, "st", (ld // 128, C), torch.float32, x.device)
     padded_offsets = _out(padded_offsets, "padded_offsets", (G + 1,), torch.int32, x.device)
     _check("quant_act_128x1_grouped_e4m3", lib.quant_act_128x1_grouped_e4m3(
         _p(x), _dtype_code(x), int(bool(swiglu_input)), x_rows, C, _p(row_index), _p(row_scale),
@@ -380,15 +380,16 @@ def quant_act_128x1_grouped_e4m3(x, group_offsets, M=None, row_index=None, row_s
 
 def grouped_wgrad_fp8(aq, as_, bq, bs, padded_offsets, out_dtype=torch.float32, c=None, accumulate=False):
     """dW [G, Na, Nb] = per-expert dOut^T . In over the 128x1-quantised operands
-    aq [Na, ld] (output gradient) and bq [Nb, ld] (input)."""
+    aq [Na, ld] (output gradient) and bq [Nb, ld] (input), scales tile-major
+    as [ld/128, Na], bs [ld/128, Nb]."""
     _need(aq, "aq", torch.uint8)
     Na, ld = aq.shape
-    _need(as_, "as", torch.float32, (Na, ld // 128))
+    _need(as_, "as", torch.float32, (ld // 128, Na))
     _need(bq, "bq", torch.uint8)
     Nb = bq.shape[0]
     if bq.shape[1] != ld:
         raise ValueError("aq and bq must share the padded row stride")
-    _need(bs, "bs", torch.float32, (Nb, ld // 128))
+    _need(bs, "bs", torch.float32, (ld // 128, Nb))
     _need(padded_offsets, "padded_offsets", torch.int32)
     G = padded_offsets.shape[0] - 1
     if c is not None and c.dtype in (torch.float32, torch.bfloat16):

@@ -21,15 +21,19 @@
 //   index (gather), optionally times a per-row factor (the combine gate, for
 //   the down projection's output gradient), or as h = silu(g) * u of a
 //   float32 gate|up row (the forward's binary32 SwiGLU).
-// wgrad_kernel           one workgroup per 128x128 output tile of one expert;
-//   4 waves of 64x64.  The tile's K is the expert's padded row count (one or
-//   two 128-row chunks at the DeepSeek-V3 shape), so the kernel streams its
-//   output: every chunk is loaded straight into registers (32 bytes per lane
-//   and operand fragment), multiplied with one
+// wgrad_kernel           one workgroup per 128x128 output tile of one expert,
+//   4 waves of 64x64, 3 waves per SIMD.  The tile's K is the expert's padded
+//   row count (one or two 128-row chunks at the DeepSeek-V3 shape), so the
+//   kernel streams its output: every chunk is loaded straight into
+//   registers (32 bytes per lane and operand fragment; staging through LDS
+//   and a persistent tile walk both measured slower, the latter because the
+//   single vector-memory counter makes each tile's prefetch wait for the
+//   previous tile's stores), multiplied with one
 //   V_MFMA_SCALE_F32_16X16X128_F8F6F4 per 16x16 block with a zero
 //   accumulator, and promoted with one FMA per output by the product of the
-//   two 128x1 scales (which now vary along both output axes).  The input
-//   operand sits on the instruction's row axis, so each lane holds 4
+//   two 128x1 scales (which vary along both output axes; stored tile-major,
+//   [padded row / 128, column], so a fragment's scales are contiguous).  The
+//   input operand sits on the instruction's row axis, so each lane holds 4
 //   consecutive input features of one output row and stores them as one
 //   16-byte (float32) or 8-byte (bf16) vector.  Tiles of one expert are
 //   consecutive and the logical tile order is dealt XCD by XCD, so an
@@ -166,7 +170,7 @@ __global__ __launch_bounds__(256) void quant128x1_kernel(
   uint8_t* dst = qt + col * ld + prow + 32 * qq;
   *reinterpret_cast<uint4*>(dst) = make_uint4(w[0], w[1], w[2], w[3]);
   *reinterpret_cast<uint4*>(dst + 16) = make_uint4(w[4], w[5], w[6], w[7]);
-  if (qq == 0) st[col * (ld / 128) + tt] = s;
+  if (qq == 0) st[(int64_t)tt * C + col] = s;
 }
 
 __device__ __forceinline__ v8i load_frag(const uint8_t* p) {
@@ -199,14 +203,13 @@ __device__ __forceinline__ void store4(uint16_t* p, const float v[4], bool acc) 
   *reinterpret_cast<uint2*>(p) = o;
 }
 
-template <typename OT>
-__global__ __launch_bounds__(256) void wgrad_kernel(const uint8_t* __restrict__ aq, const float* __restrict__ as,
-                                                    const uint8_t* __restrict__ bq, const float* __restrict__ bs,
-                                                    const int* __restrict__ poff, int Na, int Nb, int64_t ld,
-                                                    int64_t n_tiles, int64_t per_xcd, OT* __restrict__ out,
-                                                    int accumulate) {
+template <typename OT, bool kAcc>
+__global__ __launch_bounds__(256, 3) void wgrad_kernel(const uint8_t* __restrict__ aq, const float* __restrict__ as,
+                                                       const uint8_t* __restrict__ bq, const float* __restrict__ bs,
+                                                       const int* __restrict__ poff, int Na, int Nb, int64_t ld,
+                                                       int64_t n_tiles, int64_t per_xcd, OT* __restrict__ out) {
   const int64_t b = blockIdx.x;
-  const int64_t tile = (b & 7) * per_xcd + (b >> 3);
+  const int64_t tile = (b & 7) * per_xcd + (b >> 3);  // workgroup b runs on XCD b % 8
   if (tile >= n_tiles) return;
   const int to_n = Na / 128, ti_n = Nb / 128;
   const int64_t per_g = (int64_t)to_n * ti_n;
@@ -228,10 +231,8 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const uint8_t* __restrict__ 
 #pragma unroll
     for (int fo = 0; fo < 4; ++fo) acc[fi][fo] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  const uint8_t* pa = bq + (i_base + l16) * ld + 32 * q;  // In rows i_base + 16 fi + lane % 16
-  const uint8_t* pb = aq + (o_base + l16) * ld + 32 * q;  // dOut rows o_base + 16 fo + lane % 16
-  const float* sIp = bs + (i_base + 4 * q) * nkb;           // In scales of rows i_base + 16 fi + 4 q + v
-  const float* sOp = as + (o_base + l16) * nkb;             // dOut scales of rows o_base + 16 fo + lane % 16
+  const uint8_t* pa = bq + (i_base + l16) * ld + 32 * q;  // In rows i_base + 16 f + lane % 16
+  const uint8_t* pb = aq + (o_base + l16) * ld + 32 * q;  // dOut rows o_base + 16 f + lane % 16
   for (int64_t kb = kb0; kb < kb1; ++kb) {
     v8i A[4], B[4];
     float sI[4][4], sO[4];
@@ -239,9 +240,10 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const uint8_t* __restrict__ 
     for (int f = 0; f < 4; ++f) {
       A[f] = load_frag(pa + 16 * f * ld + kb * 128);
       B[f] = load_frag(pb + 16 * f * ld + kb * 128);
-      sO[f] = sOp[16 * f * nkb + kb];
-#pragma unroll
-      for (int v = 0; v < 4; ++v) sI[f][v] = sIp[(16 * f + v) * nkb + kb];
+      // tile-major scales: In rows i_base + 16 f + 4 q + v are contiguous
+      const float4 s4 = *reinterpret_cast<const float4*>(bs + kb * Nb + i_base + 16 * f + 4 * q);
+      sI[f][0] = s4.x, sI[f][1] = s4.y, sI[f][2] = s4.z, sI[f][3] = s4.w;
+      sO[f] = as[kb * Na + o_base + 16 * f + l16];
     }
     const v4f zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -259,7 +261,7 @@ __global__ __launch_bounds__(256) void wgrad_kernel(const uint8_t* __restrict__ 
 #pragma unroll
     for (int fi = 0; fi < 4; ++fi) {
       const float v[4] = {acc[fi][fo][0], acc[fi][fo][1], acc[fi][fo][2], acc[fi][fo][3]};
-      store4(og + (o_base + 16 * fo + l16) * Nb + i_base + 16 * fi + 4 * q, v, accumulate != 0);
+      store4(og + (o_base + 16 * fo + l16) * Nb + i_base + 16 * fi + 4 * q, v, kAcc);
     }
 }
 
@@ -342,11 +344,14 @@ extern "C" moe_status grouped_wgrad_fp8(const uint8_t* aq, const float* as, cons
   hipStream_t s = as_stream(stream);
   const int64_t per_xcd = (n_tiles + 7) / 8;
   const unsigned grid = (unsigned)(8 * per_xcd);
-  if (c_dtype == MOE_F32)
-    wgrad_kernel<float><<<grid, 256, 0, s>>>(aq, as, bq, bs, padded_offsets, Na, Nb, ld, n_tiles, per_xcd,
-                                             static_cast<float*>(c), accumulate);
-  else
-    wgrad_kernel<uint16_t><<<grid, 256, 0, s>>>(aq, as, bq, bs, padded_offsets, Na, Nb, ld, n_tiles, per_xcd,
-                                                static_cast<uint16_t*>(c), accumulate);
+#define MOE_WGRAD_LAUNCH(OT, ACC)                                                                          \
+  wgrad_kernel<OT, ACC><<<grid, 256, 0, s>>>(aq, as, bq, bs, padded_offsets, Na, Nb, ld, n_tiles, per_xcd, \
+                                            static_cast<OT*>(c))
+  if (c_dtype == MOE_F32) {
+    if (accumulate) MOE_WGRAD_LAUNCH(float, true); else MOE_WGRAD_LAUNCH(float, false);
+  } else {
+    if (accumulate) MOE_WGRAD_LAUNCH(uint16_t, true); else MOE_WGRAD_LAUNCH(uint16_t, false);
+  }
+#undef MOE_WGRAD_LAUNCH
   return after_launch("grouped_wgrad_fp8", s);
 }

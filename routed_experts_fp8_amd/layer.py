@@ -266,20 +266,20 @@ class MoEWeightGrad:
         ld = L.moe_wgrad_padded_rows(M, E)
         self.ld = ld
         self.buf = dict(poff=e((E + 1,), torch.int32),
-                        dc2t=e((H, ld), torch.uint8), dc2ts=e((H, ld // 128), torch.float32),
-                        ht=e((I, ld), torch.uint8), hts=e((I, ld // 128), torch.float32),
-                        d1t=e((2 * I, ld), torch.uint8), d1ts=e((2 * I, ld // 128), torch.float32),
-                        xt=e((H, ld), torch.uint8), xts=e((H, ld // 128), torch.float32),
+                        dc2t=e((H, ld), torch.uint8), dc2ts=e((ld // 128, H), torch.float32),
+                        ht=e((I, ld), torch.uint8), hts=e((ld // 128, I), torch.float32),
+                        d1t=e((2 * I, ld), torch.uint8), d1ts=e((ld // 128, 2 * I), torch.float32),
+                        xt=e((H, ld), torch.uint8), xts=e((ld // 128, H), torch.float32),
                         dw2=e((E, H, I), out_dtype), dw13=e((E, 2 * I, H), out_dtype))
         if f.shared_I:
             Is = f.shared_I
             lds = L.moe_wgrad_padded_rows(T, 1)
             self.lds = lds
             self.buf.update(spoff=e((2,), torch.int32),
-                            sdyt=e((H, lds), torch.uint8), sdyts=e((H, lds // 128), torch.float32),
-                            sht=e((Is, lds), torch.uint8), shts=e((Is, lds // 128), torch.float32),
-                            sd1t=e((2 * Is, lds), torch.uint8), sd1ts=e((2 * Is, lds // 128), torch.float32),
-                            sxt=e((H, lds), torch.uint8), sxts=e((H, lds // 128), torch.float32),
+                            sdyt=e((H, lds), torch.uint8), sdyts=e((lds // 128, H), torch.float32),
+                            sht=e((Is, lds), torch.uint8), shts=e((lds // 128, Is), torch.float32),
+                            sd1t=e((2 * Is, lds), torch.uint8), sd1ts=e((lds // 128, 2 * Is), torch.float32),
+                            sxt=e((H, lds), torch.uint8), sxts=e((lds // 128, H), torch.float32),
                             sdw2=e((1, H, Is), out_dtype), sdw13=e((1, 2 * Is, H), out_dtype))
 
     def __call__(self, x, dy, accumulate=False, on_stage=None):

@@ -23,8 +23,10 @@ def _groups(sizes):
 
 
 def _valid(qt, st, p):
+    """Codes [C, P_G] and scales [C, P_G/128] (the oracle's orientation) of
+    the GPU's [C, ld] codes and tile-major [ld/128, C] scales."""
     n = int(p[-1])
-    return np_(qt)[:, :n], np_(st)[:, :n // 128]
+    return np_(qt)[:, :n], np.ascontiguousarray(np_(st)[:n // 128, :].T)
 
 
 @pytest.mark.parametrize("kind", ["f32", "bf16_gather_scale", "swiglu", "swiglu_gather"])
@@ -91,14 +93,18 @@ def _pad_ld(a, ld):
     return out
 
 
+def _scales_dev(s, ld):
+    """Oracle scales [N, Mp/128] -> the GPU's tile-major [ld/128, N]."""
+    return to_dev(np.ascontiguousarray(_pad_ld(s, ld // 128).T))
+
+
 @pytest.mark.parametrize("sizes,Na,Nb", [([0, 5, 300, 128, 1], 256, 384), ([700], 128, 128),
                                          ([0, 0, 0], 128, 256)])
 def test_wgrad_gemm(sizes, Na, Nb):
     aq, as_, bq, bs, p = _wgrad_problem(sizes, Na, Nb)
     C, Mag = O.wgrad_gemm(aq, as_, bq, bs, p)
     ld = R.moe_wgrad_padded_rows(sum(sizes), len(sizes))
-    args = [to_dev(_pad_ld(aq, ld)), to_dev(_pad_ld(as_, ld // 128)), to_dev(_pad_ld(bq, ld)),
-            to_dev(_pad_ld(bs, ld // 128)), to_dev(p)]
+    args = [to_dev(_pad_ld(aq, ld)), _scales_dev(as_, ld), to_dev(_pad_ld(bq, ld)), _scales_dev(bs, ld), to_dev(p)]
     c = R.grouped_wgrad_fp8(*args)
     cg = np_(c).astype(np.float64)
     assert np.all(np.abs(cg - C) <= GEMM_RTOL * Mag + 1e-30)
@@ -121,8 +127,8 @@ def test_wgrad_gemm_many_groups():
     aq, as_, bq, bs, p = _wgrad_problem(sizes, 256, 512)
     C, Mag = O.wgrad_gemm(aq, as_, bq, bs, p)
     ld = R.moe_wgrad_padded_rows(sum(sizes), len(sizes))
-    c = R.grouped_wgrad_fp8(to_dev(_pad_ld(aq, ld)), to_dev(_pad_ld(as_, ld // 128)), to_dev(_pad_ld(bq, ld)),
-                            to_dev(_pad_ld(bs, ld // 128)), to_dev(p))
+    c = R.grouped_wgrad_fp8(to_dev(_pad_ld(aq, ld)), _scales_dev(as_, ld), to_dev(_pad_ld(bq, ld)),
+                            _scales_dev(bs, ld), to_dev(p))
     assert np.all(np.abs(np_(c).astype(np.float64) - C) <= GEMM_RTOL * Mag + 1e-30)
 
 
@@ -228,7 +234,7 @@ def test_fp8_chunk_accumulation_model():
     the magnitude sum."""
     vals = O.e4m3_values()
     code = {float(v): i for i, v in enumerate(vals)}
-    one = torch.ones((128, 1), dtype=torch.float32, device=dev())
+    one = torch.ones((1, 128), dtype=torch.float32, device=dev())
     p = torch.tensor([0, 128], dtype=torch.int32, device=dev())
 
     def run(arows, brow):
