@@ -18,6 +18,7 @@ region.  The CPU baseline times the oracle (test infrastructure) on a
 bounded sample of the same workload and scales it to the full layer.
 
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
+                      [--section layer|backward]
 """
 
 import argparse
@@ -43,6 +44,10 @@ def parse():
     p.add_argument("--config", default="dsv3")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true")
+    p.add_argument("--section", choices=["layer", "backward"], default="layer",
+                   help="layer: the forward bench line (default); backward: time only the input-side "
+                        "backward + weight gradients of the same workload, K steps after W warm-ups "
+                        "(for per-kernel profiles), printing their own JSON line")
     return p.parse_args()
 
 
@@ -321,6 +326,33 @@ def cpu_baseline(cfg, d, n_experts=12, shared_tokens=1024, combine_tokens=2048):
                 seconds_full_layer_estimate=total)
 
 
+def backward_section(args, cfg, d, w, torch, R, synth):
+    """K timed steps of the input-side backward followed by the FP8 weight
+    gradients (float32), with per-stage HIP events; one JSON line."""
+    T, H, E, I, K = cfg["T"], cfg["H"], cfg["E"], cfg["I"], cfg["K"]
+    dev = d["x"].device
+    wt = R.transpose_weights(w)
+    fwd = R.MoEForward(T, H, E, I, cfg["route"], w, dev, fused=False, shared_I=cfg.get("shared_I"))
+    fwd(d["x"], d["logits"], d["bias"])
+    dy = synth.output_grad(T, H, dev, seed=4)
+    bwd = R.MoEBackward(fwd, wt, weight_grad=True)
+    wg = R.MoEWeightGrad(bwd)
+
+    def step(mark):
+        bwd(dy, d["logits"], on_stage=mark)
+        wg(d["x"], dy, on_stage=mark)
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    total, st = staged(step, args.steps, torch)
+    line = {"metric": "MoE-layer input-side backward + FP8 weight gradients, tokens/s, 1 GPU",
+            "value": T / (total / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": total, "higher_is_better": True, "dtype": "fp8_e4m3",
+            "data": "synthetic", "config": {"workload": cfg["name"]}, "stages_ms": st}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -337,6 +369,9 @@ def main():
     log(f"generating {cfg['name']} inputs on the GPU")
     d = synth.layer_inputs(cfg, dev, seed=0)
     w = R.quantize_weights(d["w13"], d["w2"], d.get("sw13"), d.get("sw2"))
+    if args.section == "backward":
+        backward_section(args, cfg, d, w, torch, R, synth)
+        return
     fwd = R.MoEForward(T, H, E, I, cfg["route"], w, dev, fused=True, shared_I=cfg.get("shared_I"))
     torch.cuda.synchronize()
     log("warmup")

@@ -36,8 +36,11 @@
 //   input operand sits on the instruction's row axis, so each lane holds 4
 //   consecutive input features of one output row and stores them as one
 //   16-byte (float32) or 8-byte (bf16) vector.  Tiles of one expert are
-//   consecutive and the logical tile order is dealt XCD by XCD, so an
-//   expert's operands (a few MB) stay in one XCD's L2.
+//   consecutive and the logical tile order is dealt XCD by XCD; inside an
+//   expert the order is blocked (4 output-feature tiles by every
+//   input-feature tile), so the tiles in flight on one XCD share a few
+//   operand slabs, which stay in its L2 despite the output stream passing
+//   through it.
 #include "device_common.h"
 #include "host_common.h"
 
@@ -48,6 +51,7 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxGroups = 1024;
+constexpr int kOB = 4;  // output-feature tiles per block of the wgrad tile order (measured: 1, 2, 4, 8, 16)
 
 __global__ __launch_bounds__(256) void padded_offsets_kernel(const int* __restrict__ offsets, int G,
                                                              int* __restrict__ poff) {
@@ -215,7 +219,13 @@ __global__ __launch_bounds__(256, 3) void wgrad_kernel(const uint8_t* __restrict
   const int64_t per_g = (int64_t)to_n * ti_n;
   const int g = (int)(tile / per_g);
   const int rem = (int)(tile % per_g);
-  const int to = rem / ti_n, ti = rem % ti_n;
+  // blocked order inside the expert: blocks of kOB output-feature tiles, and
+  // inside a block the input-feature tile outermost, so the tiles an XCD runs
+  // at once share a few operand slabs of each kind instead of one A slab and
+  // every B slab (which the output stream would evict before their reuse)
+  const int ob = rem / (kOB * ti_n), r2 = rem % (kOB * ti_n);
+  const int obs = to_n - ob * kOB < kOB ? to_n - ob * kOB : kOB;  // tiles in this block
+  const int to = ob * kOB + r2 % obs, ti = r2 / obs;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int q = lane >> 4, l16 = lane & 15;
   const int64_t i_base = (int64_t)ti * 128 + (wave & 1) * 64;   // input features (instruction rows)
