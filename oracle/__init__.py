@@ -62,6 +62,7 @@ from .backward import (combine_backward, swiglu_backward, route_backward_sigmoid
                        route_backward_softmax, layer_backward)
 from .transpose import block_transpose
 from .wgrad import padded_offsets, grouped_rows, quant_act_128x1_grouped, wgrad_gemm, layer_wgrad
+from .router import router_logits, bias_update
 from .layer import layer_forward, layer_forward_dense
 
 __all__ = [
@@ -73,4 +74,5 @@ __all__ = [
     "block_transpose", "layer_forward", "layer_forward_dense", "combine_backward",
     "swiglu_backward", "route_backward_sigmoid", "route_backward_softmax", "layer_backward",
     "padded_offsets", "grouped_rows", "quant_act_128x1_grouped", "wgrad_gemm", "layer_wgrad",
+    "router_logits", "bias_update",
 ]

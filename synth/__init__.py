@@ -7,7 +7,7 @@ quantisation, routing, permutation or GEMM -- only shapes and random numbers.
 """
 
 from .configs import CONFIGS, get_config
-from .gen import tensor_seed, randn, layer_inputs, expert_weights, zipf_offsets, output_grad
+from .gen import tensor_seed, randn, layer_inputs, expert_weights, zipf_offsets, output_grad, router_weight
 
 __all__ = ["CONFIGS", "get_config", "tensor_seed", "randn", "layer_inputs",
-           "expert_weights", "zipf_offsets", "output_grad"]
+           "expert_weights", "zipf_offsets", "output_grad", "router_weight"]

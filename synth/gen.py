@@ -10,13 +10,14 @@ tensor: CPU and GPU generators give different (equally valid) streams.
 Tensor ids: 1 router logits [T, E]; 2 activations x [T, H]; 3 expert
 gate|up weights [E, 2I, H] (sub id = expert); 4 expert down weights [E, H, I]
 (sub id = expert); 5 / 6 shared expert gate|up / down; 7 expert bias [E];
-8 rank permutation for the skewed-load offsets; 9 output gradient dY.
+8 rank permutation for the skewed-load offsets; 9 output gradient dY;
+10 router projection weight [E, H].
 """
 
 import numpy as np
 import torch
 
-TID_LOGITS, TID_X, TID_W13, TID_W2, TID_SW13, TID_SW2, TID_BIAS, TID_RANK, TID_DY = range(1, 10)
+TID_LOGITS, TID_X, TID_W13, TID_W2, TID_SW13, TID_SW2, TID_BIAS, TID_RANK, TID_DY, TID_WR = range(1, 11)
 
 _DT = {"f32": torch.float32, "bf16": torch.bfloat16}
 
@@ -99,3 +100,9 @@ def output_grad(M, N, device, seed=0):
 
 __all__ = ["tensor_seed", "randn", "zipf_offsets", "expert_weights", "layer_inputs",
            "output_grad"]
+
+
+def router_weight(cfg, device, seed=0):
+    """Router projection weight [E, H] float32, N(0, 1/H), so that the logits
+    of N(0, 1) activations are about N(0, 1) like the generated logits."""
+    return randn((cfg["E"], cfg["H"]), float(cfg["H"]) ** -0.5, torch.float32, device, seed, TID_WR)
