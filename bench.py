@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
+FP32_MFMA_PEAK_TFLOPS = 157.3  # MI355X dense FP32 matrix, TFLOP/s
 METRIC = "MoE-layer fwd tokens/s + FP8 grouped-GEMM TFLOP/s (% MFMA peak), 1 GPU"
 
 
@@ -174,6 +175,21 @@ def staged(fn, reps, torch):
             stages[name] = stages.get(name, 0.0) + a.elapsed_time(b) / reps
     total = sum(step[0][1].elapsed_time(step[-1][1]) for step in marks) / reps
     return total, stages
+
+
+def router_rows(cfg, d, fwd, torch, R, synth, reps=5):
+    """Router projection (float32 matrix cores) and one balancing bias update
+    on the same workload."""
+    T, H, E = cfg["T"], cfg["H"], cfg["E"]
+    wr = synth.router_weight(cfg, d["x"].device, seed=0)
+    lg = torch.empty((T, E), dtype=torch.float32, device=d["x"].device)
+    ms = time_op(lambda: R.moe_router_logits(d["x"], wr, logits=lg), reps, torch)
+    fl = gemm_flops(T, E, H)
+    bias = torch.zeros(E, dtype=torch.float32, device=d["x"].device)
+    ms_b = time_op(lambda: R.moe_bias_update(fwd.buf["offsets"], 1e-3, bias), reps, torch)
+    return dict(router_logits=dict(ms=ms, TFLOPs=fl / ms / 1e9, frac_fp32_mfma=fl / ms / 1e9 / FP32_MFMA_PEAK_TFLOPS,
+                                   flops=fl),
+                bias_update_us=ms_b * 1e3)
 
 
 def backward_rows(cfg, d, w, torch, R, synth, reps=5):
@@ -450,6 +466,8 @@ def main():
     if not args.no_extra:
         log("extra rows: weight quantisation, block transpose, dgrad")
         extra = extra_rows(cfg, d, fwd, torch, R, synth)
+        log("router projection and bias update")
+        extra["router"] = router_rows(cfg, d, fwd, torch, R, synth)
         log("input-side backward")
         extra["backward"] = backward_rows(cfg, d, w, torch, R, synth)
         log("other workloads: MoGE and skewed-load layers")

@@ -408,6 +408,42 @@ MOE_API moe_status grouped_wgrad_fp8(const uint8_t* aq, const float* as, const u
                              const int32_t* padded_offsets, int32_t G, int32_t Na, int32_t Nb, int64_t ld,
                              void* c, moe_dtype c_dtype, int32_t accumulate, void* stream);
 
+/* ------------------------------------------------------------------------
+ * Router projection and the balancing bias.  [DSV3-MOE]: affinity scores
+ * come from the router; a per-expert bias, adjusted to balance the load
+ * instead of an auxiliary loss, shifts the top-K selection (see moe_route).
+ * ------------------------------------------------------------------------ */
+
+/*
+ * moe_router_logits -- logits = x . W_r^T in float32 (the gating path is not
+ * quantised): logits[t, e] = sum_h x[t, h] * w_router[e, h], float32 products
+ * and sums on the matrix cores (summation order unspecified; error within
+ * (H + 2) 2^-24 sum_h |x w| of the exact sum).
+ *
+ *  x_bf16    bf16 [T, H] (raw 16-bit patterns)   layer input
+ *  w_router  f32  [E, H]                          router weight
+ *  logits    f32  [T, E] (out)                    input of moe_route
+ *  H % 64 == 0, E <= 4194240.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_ALIGN
+ *         (x_bf16, w_router 16-byte).
+ */
+MOE_API moe_status moe_router_logits(const uint16_t* x_bf16, const float* w_router, int32_t T, int32_t H,
+                             int32_t E, float* logits, void* stream);
+
+/*
+ * moe_bias_update -- one step of the aux-loss-free balancing (a reading: the
+ * pages do not give the rule): with load_e = offsets[e+1] - offsets[e] (the
+ * step's grouped rows per expert, moe_permute's offsets) and the mean load
+ * (offsets[E] - offsets[0]) / E,
+ *   bias[e] = fl32(bias[e] - gamma * sign(load_e - mean)),
+ * the sign decided exactly on integers.
+ *
+ *  expert_offsets i32 [E+1] (device), gamma (by value), bias f32 [E] (in/out).
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN.
+ */
+MOE_API moe_status moe_bias_update(const int32_t* expert_offsets, int32_t E, float gamma, float* bias,
+                           void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -10,7 +10,8 @@ from ._lib import (MoeError, fp8_block_transpose, grouped_gemm_fp8_blockscaled,
                    grouped_gemm_fp8_swiglu, moe_combine, moe_combine_backward, moe_permute,
                    moe_permute_workspace_size, moe_route, moe_route_backward, quant_act_1x128_e4m3,
                    quant_weight_128x128_e4m3, swiglu, swiglu_backward, moe_wgrad_padded_rows,
-                   quant_act_128x1_grouped_e4m3, grouped_wgrad_fp8, LIB_PATH)
+                   quant_act_128x1_grouped_e4m3, grouped_wgrad_fp8, moe_router_logits, moe_bias_update,
+                   LIB_PATH)
 from .layer import MoEBackward, MoEForward, MoEWeightGrad, quantize_weights, transpose_weights
 
 __all__ = ["MoeError", "fp8_block_transpose", "grouped_gemm_fp8_blockscaled",
@@ -18,4 +19,5 @@ __all__ = ["MoeError", "fp8_block_transpose", "grouped_gemm_fp8_blockscaled",
            "moe_route", "quant_act_1x128_e4m3", "quant_weight_128x128_e4m3", "swiglu",
            "moe_combine_backward", "swiglu_backward", "moe_route_backward",
            "moe_wgrad_padded_rows", "quant_act_128x1_grouped_e4m3", "grouped_wgrad_fp8",
+           "moe_router_logits", "moe_bias_update",
            "MoEForward", "MoEBackward", "MoEWeightGrad", "quantize_weights", "transpose_weights", "LIB_PATH"]

@@ -51,6 +51,8 @@ _SIGNATURES = {
                                             _c_void_p]),
     "grouped_wgrad_fp8": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32,
                                  _i64, _c_void_p, _i32, _i32, _c_void_p]),
+    "moe_router_logits": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _i32, _c_void_p, _c_void_p]),
+    "moe_bias_update": (_i32, [_c_void_p, _i32, ctypes.c_float, _c_void_p, _c_void_p]),
 }
 
 
@@ -65,7 +67,7 @@ class MoeError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is missing: build it with `python -m routed_experts_fp8_amd.build` "
+            f"{LIB_PATH} is missing: build it with `python routed_experts_fp8_amd/build.py` (or __graft_entry__.build()) "
             "(there is no non-HIP fallback)")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in _SIGNATURES.items():
@@ -399,3 +401,26 @@ def grouped_wgrad_fp8(aq, as_, bq, bs, padded_offsets, out_dtype=torch.float32, 
         _p(aq), _p(as_), _p(bq), _p(bs), _p(padded_offsets), G, Na, Nb, ld, _p(c), _dtype_code(c),
         int(bool(accumulate)), _stream()))
     return c
+
+
+def moe_router_logits(x, w_router, logits=None):
+    """x bf16 [T, H], w_router f32 [E, H] -> logits f32 [T, E] = x . W_r^T."""
+    _need(x, "x", torch.bfloat16)
+    T, H = x.shape
+    _need(w_router, "w_router", torch.float32)
+    E = w_router.shape[0]
+    if w_router.shape[1] != H:
+        raise ValueError("w_router must be [E, H]")
+    logits = _out(logits, "logits", (T, E), torch.float32, x.device)
+    _check("moe_router_logits", lib.moe_router_logits(_p(x), _p(w_router), T, H, E, _p(logits), _stream()))
+    return logits
+
+
+def moe_bias_update(expert_offsets, gamma, bias):
+    """In place: bias[e] -= gamma * sign(load_e - mean load), loads from the
+    permutation's expert offsets."""
+    _need(expert_offsets, "expert_offsets", torch.int32)
+    E = expert_offsets.shape[0] - 1
+    _need(bias, "bias", torch.float32, (E,))
+    _check("moe_bias_update", lib.moe_bias_update(_p(expert_offsets), E, float(gamma), _p(bias), _stream()))
+    return bias

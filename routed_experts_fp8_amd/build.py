@@ -1,6 +1,7 @@
 """Build libmoefp8.so for gfx950 with hipcc (in-tree, no JIT cache).
 
-Usage: python -m routed_experts_fp8_amd.build   (or build() from Python)
+Usage: python routed_experts_fp8_amd/build.py   (or __graft_entry__.build(); importing the
+package first would load the library this script builds)
 
 Every HIP source is compiled with:
   -ffp-contract=off                       a*b+c stays two roundings; the
@@ -27,7 +28,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["status.cpp", "quant.hip", "transpose.hip", "route.hip", "permute.hip",
-           "swiglu_combine.hip", "gemm.hip", "backward.hip", "wgrad.hip"]
+           "swiglu_combine.hip", "gemm.hip", "backward.hip", "wgrad.hip", "router.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

@@ -39,7 +39,8 @@ class MoEForward:
     """Preallocated buffers for one layer shape; ``__call__`` enqueues the
     whole forward on the current stream and returns y (bf16 [T, H])."""
 
-    def __init__(self, T, H, E, I, route, weights, device, fused=True, shared_I=None, overlap_shared=True):
+    def __init__(self, T, H, E, I, route, weights, device, fused=True, shared_I=None, overlap_shared=True,
+                 router_weight=None):
         self.T, self.H, self.E, self.I = T, H, E, I
         self.route = dict(route)
         self.K = route["K"] if route["mode"] == "sigmoid_bias" else route["n_groups"] * route["k_per_group"]
@@ -61,6 +62,10 @@ class MoEForward:
         )
         if not fused:
             self.buf["c1"] = e((M, 2 * I), torch.float32)
+        # optional router projection (float32 [E, H]): logits = x . W_r^T
+        self.wr = router_weight
+        if router_weight is not None:
+            self.buf["logits"] = e((T, E), torch.float32)
         # The shared expert only needs x's FP8 codes, so it can run on a side
         # stream beside the permutation and the routed GEMMs: its GEMMs are
         # dense and compute-heavy while the routed ones stream weights from
@@ -82,14 +87,21 @@ class MoEForward:
         L.grouped_gemm_fp8_blockscaled(hq, hs, w2q, w2s, offsets, c=c2)
         mark("gemm2")
 
-    def __call__(self, x, logits, bias=None, on_stage=None):
-        """Enqueue the forward.  on_stage(name), if given, is called after each
-        stage is enqueued on the caller's stream (the bench records a HIP event
-        there).  With the shared expert on the side stream its GEMMs are not
-        marked; "shared_join" marks the caller's stream waiting for them."""
+    def __call__(self, x, logits=None, bias=None, on_stage=None):
+        """Enqueue the forward.  logits: the router logits [T, E], or None to
+        compute them from x with the router weight given at construction.
+        on_stage(name), if given, is called after each stage is enqueued on
+        the caller's stream (the bench records a HIP event there).  With the
+        shared expert on the side stream its GEMMs are not marked;
+        "shared_join" marks the caller's stream waiting for them."""
         mark = on_stage or (lambda name: None)
         b, w, r = self.buf, self.w, self.route
         shared = None
+        if logits is None:
+            if self.wr is None:
+                raise ValueError("no logits given and no router weight")
+            logits = L.moe_router_logits(x, self.wr, logits=b["logits"])
+            mark("router")
 
         def route():
             if r["mode"] == "sigmoid_bias":
@@ -139,6 +151,12 @@ class MoEForward:
         L.moe_combine(b["c2"], b["dst_row"], b["gate"], shared, out=b["y"])
         mark("combine")
         return b["y"]
+
+    def update_bias(self, bias, gamma):
+        """Aux-loss-free balancing after a step: bias[e] -= gamma * sign(load_e
+        - mean load), with the loads of the last forward's routing (in place,
+        on the current stream)."""
+        return L.moe_bias_update(self.buf["offsets"], gamma, bias)
 
 
 def transpose_weights(w):

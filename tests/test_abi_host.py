@@ -24,7 +24,7 @@ S = None                              # null stream
 
 
 def test_every_declared_symbol_is_exported():
-    assert len(DECLARED) == 18, DECLARED
+    assert len(DECLARED) == 20, DECLARED
     for name in DECLARED:
         assert hasattr(L.lib, name), name
     assert set(DECLARED) == set(L._SIGNATURES)
@@ -189,3 +189,17 @@ def test_wgrad_errors():
     assert w(P, P, PM, P, P, 4, 128, 128, 256, P, 0, 0, S) == ALIGN
     assert w(P, P, P, P, P, 4, 128, 128, 256, ctypes.c_void_p(0x10008), 0, 0, S) == ALIGN   # f32 c
     assert w(P, P, P, P, P, 1024, 262144, 262144, 256, P, 0, 0, S) == UNSUP        # tile count
+
+
+def test_router_errors():
+    r = L.lib.moe_router_logits
+    assert r(P, P, 4, 100, 8, P, S) == SHAPE                              # H % 64
+    assert r(P, P, 4, 128, 0, P, S) == SHAPE                              # E >= 1
+    assert r(P, P, 4, 128, 2 ** 31 - 1, P, S) == UNSUP
+    assert r(N0, P, 4, 128, 8, P, S) == NULL
+    assert r(PM, P, 4, 128, 8, P, S) == ALIGN
+    assert r(N0, N0, 0, 128, 8, N0, S) == OK                              # T = 0
+    b = L.lib.moe_bias_update
+    assert b(P, 0, 0.1, P, S) == SHAPE
+    assert b(N0, 8, 0.1, P, S) == NULL
+    assert b(P, 8, 0.1, ctypes.c_void_p(0x10002), S) == ALIGN
