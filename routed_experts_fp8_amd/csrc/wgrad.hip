@@ -15,7 +15,8 @@
 //
 // padded_offsets_kernel  P from the group offsets (one workgroup, block scan).
 // quant128x1_kernel      one workgroup per (128-row tile of one expert, 64
-//   columns).  The tile is staged through LDS transposed; 4 lanes per column
+//   columns).  Rows are read with 16-byte loads (4 floats or 8 bf16 per
+//   lane) and staged through LDS transposed; 4 lanes per column
 //   take the amax of 32 rows each (shuffle reduction) and each lane writes 32
 //   codes (two 16-byte stores).  Rows come from x directly, through a row
 //   index (gather), optionally times a per-row factor (the combine gate, for
@@ -88,14 +89,16 @@ __global__ __launch_bounds__(256) void padded_offsets_kernel(const int* __restri
   }
 }
 
-__device__ __forceinline__ void load4(const float* p, float v[4]) {
+// 16 bytes of x as float32 values: 4 floats or 8 bf16.
+__device__ __forceinline__ void load16(const float* p, float v[4]) {
   const float4 f = *reinterpret_cast<const float4*>(p);
   v[0] = f.x, v[1] = f.y, v[2] = f.z, v[3] = f.w;
 }
-__device__ __forceinline__ void load4(const uint16_t* p, float v[4]) {
-  const uint2 w = *reinterpret_cast<const uint2*>(p);
-  v[0] = __uint_as_float(w.x << 16), v[1] = __uint_as_float(w.x & 0xffff0000u);
-  v[2] = __uint_as_float(w.y << 16), v[3] = __uint_as_float(w.y & 0xffff0000u);
+__device__ __forceinline__ void load16(const uint16_t* p, float v[8]) {
+  const uint4 w = *reinterpret_cast<const uint4*>(p);
+  const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) v[2 * i] = __uint_as_float(u[i] << 16), v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
 }
 
 template <typename XT, bool kSwiglu>
@@ -122,34 +125,39 @@ __global__ __launch_bounds__(256) void quant128x1_kernel(
 
   const int tid = threadIdx.x;
   {
-    const int cq = tid & 15, lr = tid >> 4;
-    const int c = cb * 64 + 4 * cq;
+    // 16-byte loads: VW values per lane (4 floats or 8 bf16), TPR lanes per
+    // 64-column row, RPP rows per pass
+    constexpr int VW = 16 / sizeof(XT), TPR = 64 / VW, RPP = 256 / TPR;
+    const int cq = tid % TPR, lr = tid / TPR;
+    const int c = cb * 64 + VW * cq;
 #pragma unroll
-    for (int p = 0; p < 8; ++p) {
-      const int j = lr + 16 * p;
-      float v[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int p = 0; p < 128 / RPP; ++p) {
+      const int j = lr + RPP * p;
+      float v[VW];
+#pragma unroll
+      for (int i = 0; i < VW; ++i) v[i] = 0.f;
       if (j < n_valid) {
         int64_t r = r0 + j;
         r = r < M ? r : M - 1;
         int64_t src = row_index ? (int64_t)row_index[r] : r;
         src = src < 0 ? 0 : (src >= x_rows ? x_rows - 1 : src);
         if constexpr (kSwiglu) {
-          float gg[4], uu[4];
-          load4(x + src * ldx + c, gg);
-          load4(x + src * ldx + C + c, uu);
+          float gg[VW], uu[VW];
+          load16(x + src * ldx + c, gg);
+          load16(x + src * ldx + C + c, uu);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = spec_silu(gg[i]) * uu[i];
+          for (int i = 0; i < VW; ++i) v[i] = spec_silu(gg[i]) * uu[i];
         } else {
-          load4(x + src * ldx + c, v);
+          load16(x + src * ldx + c, v);
         }
         if (row_scale) {
           const float f = row_scale[r];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = f * v[i];
+          for (int i = 0; i < VW; ++i) v[i] = f * v[i];
         }
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) tile[4 * cq + i][j] = v[i];
+      for (int i = 0; i < VW; ++i) tile[VW * cq + i][j] = v[i];
     }
   }
   __syncthreads();
