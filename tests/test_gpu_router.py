@@ -25,7 +25,8 @@ def _check_logits(x, w):
     return float(np.max(err / (mag + 1e-300)))
 
 
-@pytest.mark.parametrize("T,H,E", [(1, 64, 1), (65, 64, 40), (300, 512, 256), (129, 7168, 64)])
+@pytest.mark.parametrize("T,H,E", [(1, 64, 1), (65, 64, 40), (300, 512, 256), (129, 7168, 64),
+                                   (8192, 128, 256), (8200, 64, 200)])      # the last two use 64-token tiles
 def test_router_logits_shapes(T, H, E):
     x = to_dev(RNG.standard_normal((T, H)).astype(F32)).to(torch.bfloat16)
     w = to_dev((RNG.standard_normal((E, H)) / np.sqrt(H)).astype(F32))
