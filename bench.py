@@ -192,6 +192,30 @@ def router_rows(cfg, d, fwd, torch, R, synth, reps=5):
                 bias_update_us=ms_b * 1e3)
 
 
+def graph_rows(torch, R, synth, reps=50):
+    """The layer forward eager vs replayed from a captured HIP graph on the
+    small shared-expert layer (T=200, H=512, 16 experts top-4), where kernel
+    launches, not the kernels, set the step time."""
+    dev = torch.device("cuda:0")
+    cfg = dict(synth.get_config("tiny"), T=200, E=16, K=4, I=256, shared_I=256, bias_std=0.01,
+               route=dict(mode="sigmoid_bias", K=4, normalize=True), x_dtype="bf16", w_dtype="bf16")
+    d = synth.layer_inputs(cfg, dev, seed=0)
+    w = R.quantize_weights(d["w13"], d["w2"], d["sw13"], d["sw2"])
+    fwd = R.MoEForward(cfg["T"], cfg["H"], cfg["E"], cfg["I"], cfg["route"], w, dev, shared_I=cfg["shared_I"])
+    eager = time_op(lambda: fwd(d["x"], d["logits"], d["bias"]), reps, torch)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fwd(d["x"], d["logits"], d["bias"])
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fwd(d["x"], d["logits"], d["bias"])
+    graph = time_op(g.replay, reps, torch)
+    return dict(workload="T=200, H=512, 16 experts top-4 + shared", eager_ms=eager, graph_replay_ms=graph)
+
+
 def backward_rows(cfg, d, w, torch, R, synth, reps=5):
     """Input-side layer backward on the same workload: the forward that keeps
     its float32 gate|up output, the block transpose of every expert's
@@ -470,6 +494,8 @@ def main():
         extra["router"] = router_rows(cfg, d, fwd, torch, R, synth)
         log("input-side backward")
         extra["backward"] = backward_rows(cfg, d, w, torch, R, synth)
+        log("small layer: eager vs HIP graph replay")
+        extra["graph"] = graph_rows(torch, R, synth)
         log("other workloads: MoGE and skewed-load layers")
         extra["other_workloads"] = other_workload_rows(torch, R, synth)
     cpu = None

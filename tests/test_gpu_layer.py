@@ -157,3 +157,37 @@ def test_layer_shared_expert_side_stream_equals_in_line():
         y = fwd(d["x"], d["logits"], d["bias"])
     torch.cuda.synchronize()
     assert np.array_equal(bf16_bits(y), bf16_bits(y2))
+
+
+def test_layer_forward_in_a_hip_graph():
+    """The forward allocates nothing and joins its side stream, so it can be
+    captured once in a HIP graph and replayed: every replay (with the
+    program's own eager work and synchronisations in between) gives the
+    eager result bit for bit, also after the inputs change in place."""
+    cfg = _variant("tiny_sigmoid_shared")
+    d, w, fwd, y_eager = run_layer(cfg, True)
+    ref = bf16_bits(y_eager)
+    x, logits, bias = d["x"].clone(), d["logits"].clone(), d["bias"].clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):          # warm-up on the capture stream
+        fwd(x, logits, bias)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        y_graph = fwd(x, logits, bias)
+    for _ in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bf16_bits(y_graph), ref)
+        fwd(d["x"], d["logits"], d["bias"])       # eager work between replays
+        torch.cuda.synchronize()
+    # new inputs written into the captured tensors: replay follows them
+    d2 = synth.layer_inputs(cfg, dev(), seed=1, weights=False)
+    ref2 = bf16_bits(fwd(d2["x"], d2["logits"], d2["bias"]))   # eager, same weights
+    assert not np.array_equal(ref2, ref)
+    x.copy_(d2["x"]), logits.copy_(d2["logits"]), bias.copy_(d2["bias"])
+    g.replay()
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_bits(y_graph), ref2)
