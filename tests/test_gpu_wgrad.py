@@ -262,3 +262,28 @@ def test_fp8_chunk_accumulation_model():
     err = np.abs(got - prod.sum(axis=1)) / np.abs(prod).sum(axis=1)
     assert np.all(err <= 7 * 2.0 ** -13)
     print("worst chunk error / magnitude sum: %.3g" % err.max())
+
+
+def test_quant_and_wgrad_at_the_group_limit():
+    """1024 experts (the limit), most with 0-3 rows and a few with more than
+    one tile: the padded-offset scan (four experts per lane), the tile ->
+    expert search and the per-expert gradients, empty experts included."""
+    G = 1024
+    sizes = RNG.integers(0, 4, G)
+    sizes[[5, 511, 1023]] = [130, 257, 1]
+    sizes[[0, 1000]] = 0
+    off = _groups(sizes)
+    M = int(off[-1])
+    dout = RNG.standard_normal((M, 128)).astype(F32)
+    inp = RNG.standard_normal((M, 256)).astype(F32)
+    aq, as_, p = O.quant_act_128x1_grouped(dout, off)
+    bq, bs, _ = O.quant_act_128x1_grouped(inp, off)
+    qt, st, pg = R.quant_act_128x1_grouped_e4m3(to_dev(dout), to_dev(off))
+    assert np.array_equal(np_(pg), p)
+    q, s = _valid(qt, st, p)
+    assert np.array_equal(q, aq) and np.array_equal(s, as_)
+    qt2, st2, _ = R.quant_act_128x1_grouped_e4m3(to_dev(inp), to_dev(off))
+    c = np_(R.grouped_wgrad_fp8(qt, st, qt2, st2, pg)).astype(np.float64)
+    C, Mag = O.wgrad_gemm(aq, as_, bq, bs, p)
+    assert np.all(np.abs(c - C) <= GEMM_RTOL * Mag + 1e-30)
+    assert np.all(c[sizes == 0] == 0)
