@@ -45,10 +45,12 @@ def parse():
     p.add_argument("--config", default="dsv3")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true")
-    p.add_argument("--section", choices=["layer", "backward"], default="layer",
+    p.add_argument("--section", choices=["layer", "backward", "train"], default="layer",
                    help="layer: the forward bench line (default); backward: time only the input-side "
                         "backward + weight gradients of the same workload, K steps after W warm-ups "
-                        "(for per-kernel profiles), printing their own JSON line")
+                        "(for per-kernel profiles); train: a whole training step of the layer (weight "
+                        "quantisation and transpose, forward, backward, weight gradients, bias update); "
+                        "the last two print their own JSON line")
     return p.parse_args()
 
 
@@ -393,6 +395,52 @@ def backward_section(args, cfg, d, w, torch, R, synth):
     print(json.dumps(line), flush=True)
 
 
+def train_section(args, cfg, d, torch, R, synth):
+    """K timed training steps of the layer: every expert's weights quantised
+    from the bf16 masters and block-transposed (once per optimizer step, as
+    the pages' all-experts quantisation kernel does), the forward keeping its
+    float32 gate|up output, the input-side backward, the FP8 weight gradients
+    (float32) and one balancing bias update.  One JSON line."""
+    T, H, E, I, K = cfg["T"], cfg["H"], cfg["E"], cfg["I"], cfg["K"]
+    dev = d["x"].device
+    w = R.quantize_weights(d["w13"], d["w2"], d.get("sw13"), d.get("sw2"))
+    wt = R.transpose_weights(w)
+    fwd = R.MoEForward(T, H, E, I, cfg["route"], w, dev, fused=False, shared_I=cfg.get("shared_I"))
+    fwd(d["x"], d["logits"], d["bias"])
+    dy = synth.output_grad(T, H, dev, seed=4)
+    bwd = R.MoEBackward(fwd, wt, weight_grad=True)
+    wg = R.MoEWeightGrad(bwd)
+    bias = d["bias"].clone()
+
+    def step(mark):
+        m = mark or (lambda name: None)
+        # every expert's weights quantised, the backward's transposed copies
+        # written by the same launches (into the same buffers every step)
+        for k in ("w13", "w2", "sw13", "sw2"):
+            if k in d:
+                R.quant_weight_128x128_e4m3(d[k], q=w[k + "q"], scale=w[k + "s"], qt=wt[k + "tq"],
+                                            scale_t=wt[k + "ts"])
+        m("quantize_and_transpose_weights")
+        fwd(d["x"], d["logits"], bias)
+        m("forward")
+        bwd(dy, d["logits"])
+        m("backward")
+        wg(d["x"], dy)
+        m("weight_gradients")
+        fwd.update_bias(bias, 1e-3)
+        m("bias_update")
+
+    for _ in range(args.warmup):
+        step(None)
+    torch.cuda.synchronize()
+    total, st = staged(step, args.steps, torch)
+    line = {"metric": "MoE-layer training step (FP8 weights, forward, backward, FP8 weight gradients), tokens/s, 1 GPU",
+            "value": T / (total / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": total, "higher_is_better": True, "dtype": "fp8_e4m3",
+            "data": "synthetic", "config": {"workload": cfg["name"]}, "stages_ms": st}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -411,6 +459,10 @@ def main():
     w = R.quantize_weights(d["w13"], d["w2"], d.get("sw13"), d.get("sw2"))
     if args.section == "backward":
         backward_section(args, cfg, d, w, torch, R, synth)
+        return
+    if args.section == "train":
+        del w
+        train_section(args, cfg, d, torch, R, synth)
         return
     fwd = R.MoEForward(T, H, E, I, cfg["route"], w, dev, fused=True, shared_I=cfg.get("shared_I"))
     torch.cuda.synchronize()

@@ -167,10 +167,16 @@ MOE_API moe_status quant_act_1x128_e4m3(const void* x, moe_dtype x_dtype, int64_
  *         anchored at (0, 0)
  *  q      u8  [G, rows, cols]            (out)
  *  scale  f32 [G, rows/128, cols/128]    (out)
+ *  qt, scale_t  u8 [G, cols, rows], f32 [G, cols/128, rows/128] (out,
+ *         optional, both or neither NULL): the same codes and scales block-
+ *         transposed in the same pass, bit-identical to fp8_block_transpose of
+ *         (q, scale) -- the backward's operand without a second read of q
+ *                                                        [KANANA-FP8]
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN.
  */
 MOE_API moe_status quant_weight_128x128_e4m3(const void* w, moe_dtype w_dtype, int32_t G, int32_t rows,
-                                     int32_t cols, uint8_t* q, float* scale, void* stream);
+                                     int32_t cols, uint8_t* q, float* scale, uint8_t* qt, float* scale_t,
+                                     void* stream);
 
 /*
  * grouped_gemm_fp8_blockscaled -- per-group C = A . B_g^T with block-scaled

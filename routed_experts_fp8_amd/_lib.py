@@ -29,7 +29,7 @@ _SIGNATURES = {
                            _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p]),
     "quant_act_1x128_e4m3": (_i32, [_c_void_p, _i32, _i64, _i32, _c_void_p, _c_void_p, _c_void_p]),
     "quant_weight_128x128_e4m3": (_i32, [_c_void_p, _i32, _i32, _i32, _i32, _c_void_p, _c_void_p,
-                                         _c_void_p]),
+                                         _c_void_p, _c_void_p, _c_void_p]),
     "grouped_gemm_fp8_blockscaled": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p, _c_void_p,
                                             _c_void_p, _i32, _i64, _i32, _i32, _c_void_p, _i32, _c_void_p]),
     "grouped_gemm_fp8_swiglu": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p, _c_void_p,
@@ -197,16 +197,23 @@ def quant_act_1x128_e4m3(x, q=None, scale=None):
     return q, scale
 
 
-def quant_weight_128x128_e4m3(w, q=None, scale=None):
-    """w float32/bf16 [G, rows, cols] -> (codes [G, rows, cols], scales [G, rows/128, cols/128])."""
+def quant_weight_128x128_e4m3(w, q=None, scale=None, transposed=False, qt=None, scale_t=None):
+    """w float32/bf16 [G, rows, cols] -> (codes [G, rows, cols], scales [G, rows/128, cols/128]);
+    with transposed=True (or qt/scale_t given) also the block-transposed codes
+    [G, cols, rows] and scales [G, cols/128, rows/128] from the same pass:
+    -> (q, scale, qt, scale_t)."""
     code = _dtype_code(w)
     _need(w, "w", w.dtype)
     G, rows, cols = w.shape
     q = _out(q, "q", (G, rows, cols), torch.uint8, w.device)
     scale = _out(scale, "scale", (G, rows // 128, cols // 128), torch.float32, w.device)
+    transposed = transposed or qt is not None or scale_t is not None
+    if transposed:
+        qt = _out(qt, "qt", (G, cols, rows), torch.uint8, w.device)
+        scale_t = _out(scale_t, "scale_t", (G, cols // 128, rows // 128), torch.float32, w.device)
     _check("quant_weight_128x128_e4m3", lib.quant_weight_128x128_e4m3(
-        _p(w), code, G, rows, cols, _p(q), _p(scale), _stream()))
-    return q, scale
+        _p(w), code, G, rows, cols, _p(q), _p(scale), _p(qt), _p(scale_t), _stream()))
+    return (q, scale, qt, scale_t) if transposed else (q, scale)
 
 
 def _gemm_operands(aq, as_, bq, bs, offsets, a_row):

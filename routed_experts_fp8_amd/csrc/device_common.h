@@ -127,4 +127,35 @@ __device__ __forceinline__ float group_max(float v) {
   return v;
 }
 
+// ---------------------------------------------------------------------------
+// Transposed write of one 128x128-byte block held in LDS (row pitch
+// kTilePitch bytes, as 32-bit words): each of 256 threads gathers a
+// 16-row x 4-column byte patch with 16 dword reads, transposes it in
+// registers with shifts and masks, and writes 4 output rows of 16 bytes
+// (8 lanes per 128-byte output row segment).  dst points at the block's first
+// output byte, dst_ld is the output row stride.  The pitch of 132 bytes
+// spreads the column-wise dword reads over the LDS banks.
+// ---------------------------------------------------------------------------
+constexpr int kTilePitch = 132;
+
+__device__ __forceinline__ void write_block_transposed(const uint32_t* tile, uint8_t* dst, int64_t dst_ld,
+                                                       int tid) {
+  const int r0 = 16 * (tid & 7);
+  const int c0 = 4 * (tid >> 3);
+  uint32_t d[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) d[j] = tile[((r0 + j) * kTilePitch + c0) / 4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t o[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const uint32_t sh = 8 * i;
+      o[jj] = ((d[4 * jj] >> sh) & 0xffu) | (((d[4 * jj + 1] >> sh) & 0xffu) << 8) |
+              (((d[4 * jj + 2] >> sh) & 0xffu) << 16) | (((d[4 * jj + 3] >> sh) & 0xffu) << 24);
+    }
+    store16_nt(dst + (int64_t)(c0 + i) * dst_ld + r0, make_uint4(o[0], o[1], o[2], o[3]));
+  }
+}
+
 }  // namespace moefp8

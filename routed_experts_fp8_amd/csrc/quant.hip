@@ -93,10 +93,11 @@ __global__ __launch_bounds__(256) void quant_act_kernel(const T* __restrict__ x,
 // across the 4 waves through LDS, then codes are written from registers.
 // Loads are 16-byte vectors; a wave covers whole 256/512-byte row segments.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, bool kT>
 __global__ __launch_bounds__(256) void quant_weight_kernel(const T* __restrict__ w, int rows,
                                                            int cols, uint8_t* __restrict__ q,
-                                                           float* __restrict__ scale) {
+                                                           float* __restrict__ scale, uint8_t* __restrict__ qt,
+                                                           float* __restrict__ scale_t) {
   constexpr int E = Vec<T>::kElems;
   constexpr int VPR = 128 / E;              // vectors per block row
   constexpr int NV = 128 * VPR / 256;       // vectors per thread
@@ -125,6 +126,7 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const T* __restrict__
   }
   amax = group_max<64>(amax);
   __shared__ float red[4];
+  __shared__ uint32_t tile[kT ? 128 * kTilePitch / 4 : 1];  // the block's codes, for the transposed copy
   if ((tid & 63) == 0) red[tid >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
@@ -137,9 +139,26 @@ __global__ __launch_bounds__(256) void quant_weight_kernel(const T* __restrict__
     const int64_t off = gbase + (int64_t)(bi * 128 + r) * cols + bj * 128 + cv * E;
     float f[E];
     Vec<T>::unpack(raw[i], f);
-    store_codes<E>(q + off, div, f);
+    uint32_t c[E / 4];
+#pragma unroll
+    for (int k = 0; k < E / 4; ++k) c[k] = quantize4(div, f[4 * k], f[4 * k + 1], f[4 * k + 2], f[4 * k + 3]);
+    if constexpr (E == 8) {
+      *reinterpret_cast<uint2*>(q + off) = make_uint2(c[0], c[1]);
+    } else {
+      *reinterpret_cast<uint32_t*>(q + off) = c[0];
+    }
+    if constexpr (kT) {
+#pragma unroll
+      for (int k = 0; k < E / 4; ++k) tile[(r * kTilePitch + cv * E) / 4 + k] = c[k];
+    }
   }
   if (tid == 0) scale[blk] = s;  // [G, rows/128, cols/128] row-major == blk order
+  if constexpr (kT) {
+    // the block transposed: qt [G, cols, rows], scale_t [G, cols/128, rows/128]
+    __syncthreads();
+    write_block_transposed(tile, qt + gbase + (int64_t)bj * 128 * rows + bi * 128, rows, tid);
+    if (tid == 0) scale_t[g * (int64_t)br * bc + (int64_t)bj * br + bi] = s;
+  }
 }
 
 }  // namespace
@@ -171,21 +190,26 @@ extern "C" moe_status quant_act_1x128_e4m3(const void* x, moe_dtype x_dtype, int
 
 extern "C" moe_status quant_weight_128x128_e4m3(const void* w, moe_dtype w_dtype, int32_t G,
                                                 int32_t rows, int32_t cols, uint8_t* q,
-                                                float* scale, void* stream) {
+                                                float* scale, uint8_t* qt, float* scale_t, void* stream) {
   clear_detail();
   MOE_REQUIRE(w_dtype == MOE_F32 || w_dtype == MOE_BF16, MOE_ERR_UNSUPPORTED, "w_dtype %d", (int)w_dtype);
   MOE_REQUIRE(G >= 0 && rows > 0 && cols > 0 && rows % 128 == 0 && cols % 128 == 0, MOE_ERR_SHAPE,
               "G=%d rows=%d cols=%d (rows, cols positive multiples of 128)", G, rows, cols);
   if (G == 0) return MOE_OK;
   MOE_REQUIRE(w && q && scale, MOE_ERR_NULL, "w, q and scale are required");
-  MOE_REQUIRE(aligned(w, 16) && aligned(q, 16) && aligned(scale, 4), MOE_ERR_ALIGN,
-              "w and q need 16-byte alignment, scale 4-byte");
+  MOE_REQUIRE((qt == nullptr) == (scale_t == nullptr), MOE_ERR_NULL, "qt and scale_t go together");
+  MOE_REQUIRE(aligned(w, 16) && aligned(q, 16) && aligned(scale, 4) && aligned(qt, 16) && aligned(scale_t, 4),
+              MOE_ERR_ALIGN, "w, q and qt need 16-byte alignment, the scales 4-byte");
   const int64_t nblk = (int64_t)G * (rows / 128) * (cols / 128);
   MOE_REQUIRE(nblk < (1LL << 31), MOE_ERR_UNSUPPORTED, "too many blocks (%lld)", (long long)nblk);
   hipStream_t st = as_stream(stream);
-  if (w_dtype == MOE_BF16)
-    quant_weight_kernel<uint16_t><<<(unsigned)nblk, 256, 0, st>>>((const uint16_t*)w, rows, cols, q, scale);
-  else
-    quant_weight_kernel<float><<<(unsigned)nblk, 256, 0, st>>>((const float*)w, rows, cols, q, scale);
+#define MOE_QW_LAUNCH(T, TR) \
+  quant_weight_kernel<T, TR><<<(unsigned)nblk, 256, 0, st>>>((const T*)w, rows, cols, q, scale, qt, scale_t)
+  if (w_dtype == MOE_BF16) {
+    if (qt) MOE_QW_LAUNCH(uint16_t, true); else MOE_QW_LAUNCH(uint16_t, false);
+  } else {
+    if (qt) MOE_QW_LAUNCH(float, true); else MOE_QW_LAUNCH(float, false);
+  }
+#undef MOE_QW_LAUNCH
   return after_launch("quant_weight_128x128_e4m3", st);
 }

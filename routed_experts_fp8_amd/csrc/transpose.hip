@@ -3,25 +3,21 @@
 // transposes the block-quantised weights instead of re-quantising).
 //
 // One 256-thread workgroup moves one 128x128-byte block: 16-byte coalesced
-// loads (8 lanes per 128-byte row segment) into LDS, then each thread
-// gathers a 16-row x 4-column byte patch with 16 dword LDS reads, transposes
-// it in registers with byte permutes, and writes 4 output rows of 16 bytes
-// (again 8 lanes per 128-byte output row segment).  The LDS row pitch of 132
-// bytes spreads the column-wise dword reads over the banks.
+// loads (8 lanes per 128-byte row segment) into LDS, then the transposed
+// write of device_common.h (16-row x 4-column byte patches per thread,
+// 16-byte stores).
 #include "device_common.h"
 #include "host_common.h"
 
 namespace moefp8 {
 namespace {
 
-constexpr int kPitch = 132;  // bytes per LDS row (128 + 4)
-
 __global__ __launch_bounds__(256) void block_transpose_kernel(const uint8_t* __restrict__ q,
                                                               const float* __restrict__ s,
                                                               int rows, int cols,
                                                               uint8_t* __restrict__ qt,
                                                               float* __restrict__ st) {
-  __shared__ uint32_t tile[128 * kPitch / 4];
+  __shared__ uint32_t tile[128 * kTilePitch / 4];
   const int bc = cols / 128, br = rows / 128;
   const int64_t blk = blockIdx.x;
   const int bj = (int)(blk % bc);
@@ -43,7 +39,7 @@ __global__ __launch_bounds__(256) void block_transpose_kernel(const uint8_t* __r
   for (int i = 0; i < 4; ++i) {
     const int id = i * 256 + tid;
     const int r = id >> 3, c16 = id & 7;
-    uint32_t* p = tile + (r * kPitch + c16 * 16) / 4;
+    uint32_t* p = tile + (r * kTilePitch + c16 * 16) / 4;
     p[0] = in[i].x;
     p[1] = in[i].y;
     p[2] = in[i].z;
@@ -51,25 +47,7 @@ __global__ __launch_bounds__(256) void block_transpose_kernel(const uint8_t* __r
   }
   __syncthreads();
 
-  // Output patch: input rows r0..r0+15 (output byte columns), input columns
-  // c0..c0+3 (output rows).  Lanes 0..7 of each 8-lane group cover one whole
-  // 128-byte output row segment.
-  const int r0 = 16 * (tid & 7);
-  const int c0 = 4 * (tid >> 3);
-  uint32_t d[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) d[j] = tile[((r0 + j) * kPitch + c0) / 4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t o[4];
-#pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const uint32_t sh = 8 * i;
-      o[jj] = ((d[4 * jj] >> sh) & 0xffu) | (((d[4 * jj + 1] >> sh) & 0xffu) << 8) |
-              (((d[4 * jj + 2] >> sh) & 0xffu) << 16) | (((d[4 * jj + 3] >> sh) & 0xffu) << 24);
-    }
-    store16_nt(dst + (int64_t)(c0 + i) * rows + r0, make_uint4(o[0], o[1], o[2], o[3]));
-  }
+  write_block_transposed(tile, dst, rows, tid);
   if (tid == 0) {
     // scale grid: s[g][bi][bj] -> st[g][bj][bi]
     st[g * (int64_t)br * bc + (int64_t)bj * br + bi] = s[blk];

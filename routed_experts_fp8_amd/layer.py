@@ -24,15 +24,19 @@ import torch
 from . import _lib as L
 
 
-def quantize_weights(w13, w2, sw13=None, sw2=None):
-    """All experts' 128x128-block FP8 weights in one launch per matrix."""
-    q = {}
-    q["w13q"], q["w13s"] = L.quant_weight_128x128_e4m3(w13)
-    q["w2q"], q["w2s"] = L.quant_weight_128x128_e4m3(w2)
-    if sw13 is not None:
-        q["sw13q"], q["sw13s"] = L.quant_weight_128x128_e4m3(sw13)
-        q["sw2q"], q["sw2s"] = L.quant_weight_128x128_e4m3(sw2)
-    return q
+def quantize_weights(w13, w2, sw13=None, sw2=None, transposed=False):
+    """All experts' 128x128-block FP8 weights in one launch per matrix.  With
+    transposed=True the same launches also write the block-transposed copies
+    the backward uses ([KANANA-FP8]) -> (weights, transposed weights), the
+    latter in the layout of transpose_weights."""
+    q, t = {}, {}
+    mats = [("w13", w13), ("w2", w2)] + ([("sw13", sw13), ("sw2", sw2)] if sw13 is not None else [])
+    for k, m in mats:
+        r = L.quant_weight_128x128_e4m3(m, transposed=transposed)
+        q[k + "q"], q[k + "s"] = r[0], r[1]
+        if transposed:
+            t[k + "tq"], t[k + "ts"] = r[2], r[3]
+    return (q, t) if transposed else q
 
 
 class MoEForward:

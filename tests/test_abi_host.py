@@ -59,11 +59,13 @@ def test_quant_errors():
     assert f(PM, 1, 4, 128, P, P, S) == ALIGN
     assert f(N0, 0, 0, 128, N0, N0, S) == OK          # empty: nothing to do
     g = L.lib.quant_weight_128x128_e4m3
-    assert g(P, 0, 2, 100, 128, P, P, S) == SHAPE
-    assert g(P, 0, 2, 128, 130, P, P, S) == SHAPE
-    assert g(P, 0, 2, 128, 128, N0, P, S) == NULL
-    assert g(P, 0, 2, 128, 128, PM, P, S) == ALIGN
-    assert g(N0, 0, 0, 128, 128, N0, N0, S) == OK
+    assert g(P, 0, 2, 100, 128, P, P, N0, N0, S) == SHAPE
+    assert g(P, 0, 2, 128, 130, P, P, N0, N0, S) == SHAPE
+    assert g(P, 0, 2, 128, 128, N0, P, N0, N0, S) == NULL
+    assert g(P, 0, 2, 128, 128, P, P, P, N0, S) == NULL                  # qt without scale_t
+    assert g(P, 0, 2, 128, 128, PM, P, N0, N0, S) == ALIGN
+    assert g(P, 0, 2, 128, 128, P, P, PM, P, S) == ALIGN                 # qt 16-byte
+    assert g(N0, 0, 0, 128, 128, N0, N0, N0, N0, S) == OK
 
 
 def test_route_errors():

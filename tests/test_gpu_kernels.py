@@ -123,6 +123,24 @@ def test_block_transpose_bitexact(G, rows, cols):
     assert np.array_equal(np_(q2), q) and np.array_equal(np_(s2), s)
 
 
+@pytest.mark.parametrize("G,rows,cols", [(1, 128, 128), (3, 256, 640), (2, 512, 128)])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+def test_quant_weight_with_transposed_copy(G, rows, cols, dtype):
+    """The weight quantisation writing the block-transposed copy in the same
+    pass: the forward codes as without it, the copy equal to the oracle's
+    transpose of the oracle's codes and to the separate transpose kernel."""
+    w = (RNG.standard_normal((G, rows, cols)) * 0.02).astype(np.float32)
+    w[0, :128, :128] = 0.0
+    wt = to_dev(w).to(dtype)
+    q, s, qt, st = R.quant_weight_128x128_e4m3(wt, transposed=True)
+    qo, so = O.quant_weight_128x128(np_(wt))
+    assert np.array_equal(np_(q), qo) and np.array_equal(np_(s), so)
+    qto, sto = O.block_transpose(qo, so)
+    assert np.array_equal(np_(qt), qto) and np.array_equal(np_(st), sto)
+    qt2, st2 = R.fp8_block_transpose(q, s)
+    assert torch.equal(qt, qt2) and torch.equal(st, st2)
+
+
 def test_block_transpose_equals_requantised_transpose():
     w = (RNG.standard_normal((2, 256, 384)) * 0.006).astype(np.float32)
     q, s = R.quant_weight_128x128_e4m3(to_dev(w))
