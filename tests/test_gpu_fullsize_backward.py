@@ -1,6 +1,7 @@
 """Parity of the input-side backward and the FP8 weight gradients at the full
 DeepSeek-V3 layer size, in the launch configuration the bench times
-(MoEForward with its float32 gate|up output kept, MoEBackward, MoEWeightGrad),
+(weights quantised with their transposed copies in one pass, MoEForward with
+its float32 gate|up output kept, MoEBackward, MoEWeightGrad),
 checked on every grouped row of sampled experts (the least and most loaded
 ones and a random one) against the oracle's own chain for those experts:
 its own quantised weights, forward rows, combine gradient, dgrad GEMMs,
@@ -55,11 +56,12 @@ def test_fullsize_dsv3_backward_and_weight_gradients():
     cfg = synth.get_config("dsv3")
     T, H, E, I, K = cfg["T"], cfg["H"], cfg["E"], cfg["I"], cfg["K"]
     d = synth.layer_inputs(cfg, dev(), seed=0)
-    w = R.quantize_weights(d["w13"], d["w2"], d.get("sw13"), d.get("sw2"))
+    # the training-step path: quantisation writing the transposed copies too
+    w, wt = R.quantize_weights(d["w13"], d["w2"], d.get("sw13"), d.get("sw2"), transposed=True)
     fwd = R.MoEForward(T, H, E, I, cfg["route"], w, dev(), fused=False, shared_I=cfg.get("shared_I"))
     fwd(d["x"], d["logits"], d["bias"])
     dy = synth.output_grad(T, H, dev(), seed=4)
-    bwd = R.MoEBackward(fwd, R.transpose_weights(w), weight_grad=True)
+    bwd = R.MoEBackward(fwd, wt, weight_grad=True)
     bwd(dy, d["logits"])
     wg = R.MoEWeightGrad(bwd)
     out = wg(d["x"], dy)
