@@ -395,6 +395,69 @@ def backward_section(args, cfg, d, w, torch, R, synth):
     print(json.dumps(line), flush=True)
 
 
+def cpu_baseline_train(cfg, d, dy, n_experts=2):
+    """The oracle's training step on a bounded sample, scaled to the layer:
+    routing, activation quantisation and permutation of all tokens; for
+    `n_experts` median-load experts, their weights quantised and transposed,
+    the forward rows (GEMM1, SwiGLU, GEMM2), the combine gradient, both dgrad
+    GEMMs, the SwiGLU backward and both FP8 weight gradients (scaled by
+    experts); the bias update."""
+    import numpy as np
+    import oracle as O
+    from threadpoolctl import threadpool_info
+    T, H, E, I, K = cfg["T"], cfg["H"], cfg["E"], cfg["I"], cfg["K"]
+    x = d["x"].float().cpu().numpy()
+    logits = d["logits"].cpu().numpy()
+    bias = d["bias"].cpu().numpy()
+    dyn = dy.float().cpu().numpy()
+    t0 = time.perf_counter()
+    idx, gate = O.route_sigmoid_bias(logits, bias, K, True)
+    perm = O.permute(idx, E)
+    t_all = time.perf_counter() - t0
+    off, src, dst = perm["offsets"], perm["src_token"], perm["dst_row"]
+    gate_row = np.zeros(T * K, np.float32)
+    gate_row[dst.ravel()] = gate.ravel()
+    order = np.argsort(np.diff(off))
+    experts = [int(e) for e in order[len(order) // 2: len(order) // 2 + n_experts]]
+    t_exp = 0.0
+    for e in experts:
+        w13 = d["w13"][e:e + 1].float().cpu().numpy()
+        w2 = d["w2"][e:e + 1].float().cpu().numpy()
+        rows = np.arange(off[e], off[e + 1])
+        one = np.array([0, len(rows)], np.int32)
+        t0 = time.perf_counter()
+        q13, s13 = O.quant_weight_128x128(w13)
+        q2, s2 = O.quant_weight_128x128(w2)
+        q13t, s13t = O.block_transpose(q13, s13)
+        q2t, s2t = O.block_transpose(q2, s2)
+        aq, as_ = O.quant_act_1x128(x[src[rows]])
+        c1, _ = O.grouped_gemm(aq, as_, q13, s13, one, with_mag=False)
+        hq, hs, h = O.swiglu_quant(c1.astype(np.float32))
+        O.grouped_gemm(hq, hs, q2, s2, one, with_mag=False)
+        dc2 = (gate_row[rows][:, None] * dyn[src[rows]]).astype(np.float32)
+        dc2q, dc2s = O.quant_act_1x128(dc2)
+        dh, _ = O.grouped_gemm(dc2q, dc2s, q2t, s2t, one, with_mag=False)
+        dq1, ds1, d1 = O.swiglu_backward(c1.astype(np.float32), dh.astype(np.float32))
+        O.grouped_gemm(dq1, ds1, q13t, s13t, one, with_mag=False)
+        a2, s_a2, p = O.quant_act_128x1_grouped(dc2, one)
+        b2, s_b2, _ = O.quant_act_128x1_grouped(h, one)
+        O.wgrad_gemm(a2, s_a2, b2, s_b2, p, with_mag=False)
+        a1, s_a1, _ = O.quant_act_128x1_grouped(d1, one)
+        b1, s_b1, _ = O.quant_act_128x1_grouped(x[src[rows]], one)
+        O.wgrad_gemm(a1, s_a1, b1, s_b1, p, with_mag=False)
+        t_exp += time.perf_counter() - t0
+    t0 = time.perf_counter()
+    O.bias_update(bias, off, np.float32(1e-3))
+    t_all += time.perf_counter() - t0
+    total = t_all + t_exp * E / n_experts
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return dict(value=T / total, unit="tokens/s", cores=threads, kind="oracle",
+                sample=(f"oracle training step on the {cfg['name']} workload: routing, permutation and bias "
+                        f"update of all {T} tokens; weights, forward rows, backward rows and weight gradients of "
+                        f"{n_experts} median-load experts, scaled by experts (shared expert and combine not "
+                        f"included); {t_all + t_exp:.1f} s measured, {total:.0f} s estimated for the step"))
+
+
 def train_section(args, cfg, d, torch, R, synth):
     """K timed training steps of the layer: every expert's weights quantised
     from the bf16 masters and block-transposed (once per optimizer step, as
@@ -434,10 +497,11 @@ def train_section(args, cfg, d, torch, R, synth):
         step(None)
     torch.cuda.synchronize()
     total, st = staged(step, args.steps, torch)
+    cpu = None if args.no_cpu_baseline else cpu_baseline_train(cfg, d, dy)
     line = {"metric": "MoE-layer training step (FP8 weights, forward, backward, FP8 weight gradients), tokens/s, 1 GPU",
             "value": T / (total / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": total, "higher_is_better": True, "dtype": "fp8_e4m3",
-            "data": "synthetic", "config": {"workload": cfg["name"]}, "stages_ms": st}
+            "data": "synthetic", "config": {"workload": cfg["name"]}, "stages_ms": st, "cpu_baseline": cpu}
     print(json.dumps(line), flush=True)
 
 
