@@ -87,8 +87,8 @@ MOE_API const char* moe_last_error_detail(void);
 /*
  * moe_route -- token -> expert selection.            [DSV3-MOE], [PANGU-MOGE]
  *
- *  logits     f32 [T, E]   router scores (the router projection itself is
- *                          outside this library)
+ *  logits     f32 [T, E]   router scores (from moe_router_logits or the
+ *                          caller's own projection)
  *  bias       f32 [E] or NULL (= zeros); SIGMOID_BIAS only
  *  T >= 0, 1 <= E <= 1024
  *  SIGMOID_BIAS: 1 <= K <= E; n_groups and k_per_group are ignored.
@@ -429,7 +429,7 @@ MOE_API moe_status grouped_wgrad_fp8(const uint8_t* aq, const float* as, const u
  *  x_bf16    bf16 [T, H] (raw 16-bit patterns)   layer input
  *  w_router  f32  [E, H]                          router weight
  *  logits    f32  [T, E] (out)                    input of moe_route
- *  H % 64 == 0, E <= 4194240.
+ *  T >= 0 (T == 0 launches nothing), H % 64 == 0, 1 <= E <= 4194240.
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_ALIGN
  *         (x_bf16, w_router 16-byte).
  */
