@@ -53,16 +53,13 @@
 //    matching gate and up rows, so h = silu(g) * u forms in registers, the
 //    1x128 amax of h along I is reduced across lanes and the 4 row-waves
 //    through LDS, and only h's FP8 codes and scales are written.
-#include "device_common.h"
 #include "host_common.h"
+#include "lds_dma.h"
 
 #include <type_traits>
 
 namespace moefp8 {
 namespace {
-
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
 
 enum { OUT_F32 = 0, OUT_BF16 = 1, OUT_SWIGLU = 2 };
 
@@ -83,59 +80,6 @@ constexpr int kDmaPerChunk = 7;                  // per wave, see the memory pip
 constexpr int kMaxTilesPerWG = 64;              // tile-list entries per workgroup
 constexpr int kMaxNTiles = 2048;                 // n_tile field width of a tile-list entry
 constexpr int kPersistentMaxKB = 32;             // persistent launch for K <= 4096
-
-// LDS byte address of a __shared__ location.
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void*)p));
-}
-
-// Direct global -> LDS loads (gfx950 global_load_lds_dword[x4]): lane i's
-// 16 (4) bytes, read from sbase + voff_i (scalar base, per-lane 32-bit
-// offset), land at LDS address `lds` + 16 i (4 i).  Issued from inline
-// assembly so that the compiler's wait-count pass does not track them: its
-// alias tracking of LDS DMA is coarse and would otherwise force every LDS
-// read in the K loop to wait for ALL outstanding DMA, serialising the ring.
-// The kernel waits for these loads itself (s_waitcnt vmcnt + s_barrier): no
-// compiler-visible vector loads are in flight while they are, and the
-// epilogue's stores can only delay a wait, never satisfy it early (loads
-// complete in issue order, and every store adds to the count).  The
-// instructions have no destination registers; the address VGPRs are read
-// at issue.
-__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2" : : "s"(lds), "v"(voff), "s"(sbase)
-               : "memory", "m0");
-}
-__device__ __forceinline__ void dma4(const void* sbase, uint32_t voff, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, %2" : : "s"(lds), "v"(voff), "s"(sbase)
-               : "memory", "m0");
-}
-
-// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
-// accesses, not for its vector-memory loads (the ring's DMA stays in flight).
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-__device__ __forceinline__ v4f mfma_chunk(const v8i& a, const v8i& b) {
-  const v4f zero = {0.f, 0.f, 0.f, 0.f};
-  // FP8 E4M3 x FP8 E4M3 (format selectors 0, 0), no block-exponent scaling.
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, zero, 0, 0, 0, 0, 0, 0);
-}
-
-// Byte offset of logical 16-byte piece c16 of row r inside a [rows][128 B] tile.
-__device__ __forceinline__ int swz(int r, int c16) { return r * 128 + ((c16 ^ (r & 7)) << 4); }
-
-// Operand rows are always 16 r0 + lane % 16, so row & 7 == lane & 7 and the
-// swizzled byte offsets of the lane's two 16-byte pieces (logical pieces 2q
-// and 2q + 1 of its row, q = lane / 16) are the same for every row:
-// lane_lo = 128 (lane % 16) + 16 (2q ^ (lane & 7)), lane_hi = lane_lo ^ 16.
-// The row block then enters as an immediate offset.
-__device__ __forceinline__ v8i lds_operand(const uint8_t* rows16, uint32_t lane_lo, uint32_t lane_hi) {
-  const u32x4 lo = *reinterpret_cast<const u32x4*>(rows16 + lane_lo);
-  const u32x4 hi = *reinterpret_cast<const u32x4*>(rows16 + lane_hi);
-  v8i v;
-  v[0] = lo[0]; v[1] = lo[1]; v[2] = lo[2]; v[3] = lo[3];
-  v[4] = hi[0]; v[5] = hi[1]; v[6] = hi[2]; v[7] = hi[3];
-  return v;
-}
 
 template <int MODE>
 __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
@@ -305,7 +249,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
   };
 
   // ---- wave geometry ----
-  const uint32_t lane_lo = l16 * 128 + (((2 * q) ^ (l16 & 7)) << 4);
+  const uint32_t lane_lo = frag_lane_lo(lane);
   const uint32_t lane_hi = lane_lo ^ 16;
   // first weight row of instruction tile i (rows 16 i' + lane % 16)
   auto brow0 = [&](int i) { return kFused ? (i < 2 ? 0 : 128) + 32 * wn + 16 * (i & 1) : 64 * wn + 16 * i; };
@@ -338,7 +282,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
     for (int kb = 0; kb < KB; ++kb) {
       // this wave's loads of the chunk in stage cst have landed (only the next
       // chunk's may still fly; loads complete in issue order) ...
-      __builtin_amdgcn_s_waitcnt(0x0F70 | kDmaPerChunk);
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDmaPerChunk));
       // ... and every other wave's too; all waves are also done with the
       // previous chunk, whose stage receives the chunk after next now
       __builtin_amdgcn_s_barrier();
@@ -440,7 +384,7 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
     }
   }
   // the trailing re-fetches must land before the workgroup's LDS is released
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
 // Compute units of the current device (cached per device).

@@ -22,18 +22,22 @@
 //   index (gather), optionally times a per-row factor (the combine gate, for
 //   the down projection's output gradient), or as h = silu(g) * u of a
 //   float32 gate|up row (the forward's binary32 SwiGLU).
-// wgrad_kernel           one workgroup per 128x128 output tile of one expert,
-//   4 waves of 64x64, 3 waves per SIMD.  The tile's K is the expert's padded
-//   row count (one or two 128-row chunks at the DeepSeek-V3 shape), so the
-//   kernel streams its output: every chunk is loaded straight into
-//   registers (32 bytes per lane and operand fragment; staging through LDS
-//   and a persistent tile walk both measured slower, the latter because the
-//   single vector-memory counter makes each tile's prefetch wait for the
-//   previous tile's stores), multiplied with one
+// wgrad_kernel           one workgroup per 256x256 output tile of one expert,
+//   8 waves of 128 (input features) x 64 (output features), 2 waves per
+//   SIMD.  The tile's K is the expert's padded row count (one or two
+//   128-row chunks at the DeepSeek-V3 shape), so the kernel streams its
+//   output, and what bounds it is the traffic through each compute unit's
+//   vector-memory path (operand loads plus the float32 output).  Each
+//   chunk's operand rows and scales go straight from global memory into a
+//   2-stage LDS ring (global_load_lds, no register staging; 128-byte rows
+//   with the 16-byte XOR swizzle of the forward GEMM), so a workgroup reads
+//   each operand byte once: (256 + 256) x 128 bytes per chunk for 256 x 256
+//   outputs, against twice that per 128 x 128 outputs when every wave loads
+//   its own fragments.  Every chunk is multiplied with one
 //   V_MFMA_SCALE_F32_16X16X128_F8F6F4 per 16x16 block with a zero
-//   accumulator, and promoted with one FMA per output by the product of the
+//   accumulator and promoted with one FMA per output by the product of the
 //   two 128x1 scales (which vary along both output axes; stored tile-major,
-//   [padded row / 128, column], so a fragment's scales are contiguous).  The
+//   [padded row / 128, column], so a chunk's scales are contiguous).  The
 //   input operand sits on the instruction's row axis, so each lane holds 4
 //   consecutive input features of one output row and stores them as one
 //   16-byte (float32) or 8-byte (bf16) vector.  Tiles of one expert are
@@ -41,18 +45,27 @@
 //   expert the order is blocked (4 output-feature tiles by every
 //   input-feature tile), so the tiles in flight on one XCD share a few
 //   operand slabs, which stay in its L2 despite the output stream passing
-//   through it.
-#include "device_common.h"
+//   through it.  One tile per workgroup: a persistent walk would have to
+//   wait for the next tile's loads behind the previous tile's stores (one
+//   vector-memory counter counts both).
 #include "host_common.h"
+#include "lds_dma.h"
 
 namespace moefp8 {
 namespace {
 
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v4f __attribute__((ext_vector_type(4)));
-
 constexpr int kMaxGroups = 1024;
-constexpr int kOB = 4;  // output-feature tiles per block of the wgrad tile order (measured: 1, 2, 4, 8, 16)
+constexpr int kOB = 4;  // output-feature tiles per block of the wgrad tile order
+
+// wgrad_kernel: 256 x 256 output tiles, 8 waves, a 2-stage LDS ring
+constexpr int kWgThreads = 512;
+constexpr int kWgTile = 256;
+constexpr int kWgOffIn = 0;                              // [256 In rows][128 B]
+constexpr int kWgOffOut = kWgTile * 128;                 // [256 Out rows][128 B]
+constexpr int kWgOffSIn = 2 * kWgTile * 128;             // [256] float In scales
+constexpr int kWgOffSOut = kWgOffSIn + 4 * kWgTile;      // [256] float Out scales
+constexpr int kWgStageBytes = kWgOffSOut + 4 * kWgTile;  // 67584; 2 stages = 135168 B of LDS
+constexpr int kWgDmaPerChunk = 9;                        // per wave: 4 + 4 row slices, 1 scale slice
 
 __global__ __launch_bounds__(256) void padded_offsets_kernel(const int* __restrict__ offsets, int G,
                                                              int* __restrict__ poff) {
@@ -185,15 +198,6 @@ __global__ __launch_bounds__(256) void quant128x1_kernel(
   if (qq == 0) st[(int64_t)tt * C + col] = s;
 }
 
-__device__ __forceinline__ v8i load_frag(const uint8_t* p) {
-  const uint4 a = *reinterpret_cast<const uint4*>(p);
-  const uint4 b = *reinterpret_cast<const uint4*>(p + 16);
-  v8i r;
-  r[0] = (int)a.x, r[1] = (int)a.y, r[2] = (int)a.z, r[3] = (int)a.w;
-  r[4] = (int)b.x, r[5] = (int)b.y, r[6] = (int)b.z, r[7] = (int)b.w;
-  return r;
-}
-
 __device__ __forceinline__ void store4(float* p, const float v[4], bool acc) {
   float4 o = make_float4(v[0], v[1], v[2], v[3]);
   if (acc) {
@@ -216,14 +220,18 @@ __device__ __forceinline__ void store4(uint16_t* p, const float v[4], bool acc) 
 }
 
 template <typename OT, bool kAcc>
-__global__ __launch_bounds__(256, 3) void wgrad_kernel(const uint8_t* __restrict__ aq, const float* __restrict__ as,
-                                                       const uint8_t* __restrict__ bq, const float* __restrict__ bs,
-                                                       const int* __restrict__ poff, int Na, int Nb, int64_t ld,
-                                                       int64_t n_tiles, int64_t per_xcd, OT* __restrict__ out) {
+__global__ __launch_bounds__(kWgThreads, 2) void wgrad_kernel(const uint8_t* __restrict__ aq,
+                                                             const float* __restrict__ as,
+                                                             const uint8_t* __restrict__ bq,
+                                                             const float* __restrict__ bs,
+                                                             const int* __restrict__ poff, int Na, int Nb,
+                                                             int64_t ld, int64_t n_tiles, int64_t per_xcd,
+                                                             OT* __restrict__ out) {
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[2 * kWgStageBytes];
   const int64_t b = blockIdx.x;
   const int64_t tile = (b & 7) * per_xcd + (b >> 3);  // workgroup b runs on XCD b % 8
   if (tile >= n_tiles) return;
-  const int to_n = Na / 128, ti_n = Nb / 128;
+  const int to_n = (Na + kWgTile - 1) / kWgTile, ti_n = (Nb + kWgTile - 1) / kWgTile;
   const int64_t per_g = (int64_t)to_n * ti_n;
   const int g = (int)(tile / per_g);
   const int rem = (int)(tile % per_g);
@@ -233,54 +241,111 @@ __global__ __launch_bounds__(256, 3) void wgrad_kernel(const uint8_t* __restrict
   // every B slab (which the output stream would evict before their reuse)
   const int ob = rem / (kOB * ti_n), r2 = rem % (kOB * ti_n);
   const int obs = to_n - ob * kOB < kOB ? to_n - ob * kOB : kOB;  // tiles in this block
-  const int to = ob * kOB + r2 % obs, ti = r2 / obs;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int o0 = (ob * kOB + r2 % obs) * kWgTile, i0 = (r2 / obs) * kWgTile;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform wave index
   const int q = lane >> 4, l16 = lane & 15;
-  const int64_t i_base = (int64_t)ti * 128 + (wave & 1) * 64;   // input features (instruction rows)
-  const int64_t o_base = (int64_t)to * 128 + (wave >> 1) * 64;  // output features (instruction columns)
   const int64_t nkb = ld / 128;
   int64_t kb0 = poff[g] / 128, kb1 = poff[g + 1] / 128;
   kb0 = kb0 < 0 ? 0 : (kb0 > nkb ? nkb : kb0);
   kb1 = kb1 < kb0 ? kb0 : (kb1 > nkb ? nkb : kb1);
+  const int nk = (int)(kb1 - kb0);
 
-  v4f acc[4][4];
+  // ---- issue side: wave w fetches In rows and Out rows 32w .. 32w + 31 of
+  // the tile (4 slices of 8 rows each) and one scale slice; rows past Nb / Na
+  // re-read the last row.  Lane: row 8j + lane / 8 of slice j, physical
+  // 16-byte piece lane % 8, holding the swizzled logical piece.
+  const int rsub = lane >> 3, c16 = (lane & 7) ^ rsub;
+  int64_t in_row[4], out_row[4];  // scalar: first (clamped) row of each slice
+  uint32_t in_off[4], out_off[4];
 #pragma unroll
-  for (int fi = 0; fi < 4; ++fi)
+  for (int j = 0; j < 4; ++j) {
+    const int r = 32 * w + 8 * j;
+    const int ri = min(i0 + r, Nb - 1), ro = min(o0 + r, Na - 1);
+    in_row[j] = (int64_t)ri * ld;
+    out_row[j] = (int64_t)ro * ld;
+    in_off[j] = (uint32_t)((int64_t)(min(i0 + r + rsub, Nb - 1) - ri) * ld + c16 * 16);
+    out_off[j] = (uint32_t)((int64_t)(min(o0 + r + rsub, Na - 1) - ro) * ld + c16 * 16);
+  }
+  // scales: waves 0-3 fetch In scales 64w .., waves 4-7 Out scales 64(w - 4) ..
+  const bool s_in = w < 4;
+  const int s_n = s_in ? Nb : Na;
+  const int s_first = min((s_in ? i0 : o0) + 64 * (w & 3), s_n - 1);
+  const uint32_t s_off = (uint32_t)(min((s_in ? i0 : o0) + 64 * (w & 3) + lane, s_n - 1) - s_first) * 4u;
+  const float* s_src = (s_in ? bs : as) + s_first;
+  const uint32_t s_lds = (s_in ? kWgOffSIn : kWgOffSOut) + 256 * (w & 3);
+  const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(ring));
+  auto issue = [&](int64_t kb, int stage) {
+    const uint32_t st = ring_lds + stage * kWgStageBytes;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma16(bq + in_row[j] + kb * 128, in_off[j], st + kWgOffIn + (4 * w + j) * 1024);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) dma16(aq + out_row[j] + kb * 128, out_off[j], st + kWgOffOut + (4 * w + j) * 1024);
+    dma4(s_src + kb * s_n, s_off, st + s_lds);
+  };
+
+  // ---- multiply side: wave w owns In rows wi .. wi + 127 (instruction rows,
+  // 8 fragments) by Out rows wo .. wo + 63 (instruction columns, 4 fragments)
+  const int wi = (w & 1) * 128, wo = (w >> 1) * 64;
+  const uint32_t lane_lo = frag_lane_lo(lane), lane_hi = lane_lo ^ 16;
+  v4f acc[8][4];
+#pragma unroll
+  for (int fi = 0; fi < 8; ++fi)
 #pragma unroll
     for (int fo = 0; fo < 4; ++fo) acc[fi][fo] = v4f{0.f, 0.f, 0.f, 0.f};
 
-  const uint8_t* pa = bq + (i_base + l16) * ld + 32 * q;  // In rows i_base + 16 f + lane % 16
-  const uint8_t* pb = aq + (o_base + l16) * ld + 32 * q;  // dOut rows o_base + 16 f + lane % 16
-  for (int64_t kb = kb0; kb < kb1; ++kb) {
-    v8i A[4], B[4];
-    float sI[4][4], sO[4];
+  // two stages: chunks 0 and 1 are issued up front, chunk c + 1 (c >= 1) once
+  // every wave is done with chunk c - 1, whose stage it takes
+  if (nk > 0) issue(kb0, 0);
+  if (nk > 1) issue(kb0 + 1, 1);
+  for (int c = 0; c < nk; ++c) {
+    // this wave's loads of chunk c have landed (chunk 1 may still fly at c = 0;
+    // loads complete in issue order) and its reads of chunk c - 1 are done;
+    // after the barrier the same holds for every wave.  The asm's memory
+    // clobber keeps the LDS reads below on this side of it.
+    static_assert(kWgDmaPerChunk == 9, "the wait below counts one chunk's loads");
+    if (c == 0 && nk > 1)
+      asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (c >= 1 && c + 1 < nk) issue(kb0 + c + 1, (c + 1) & 1);
+    const uint8_t* st = ring + (c & 1) * kWgStageBytes;
+    const float* sSI = reinterpret_cast<const float*>(st + kWgOffSIn);
+    const float* sSO = reinterpret_cast<const float*>(st + kWgOffSOut);
+    v8i bo[4];
+    float so[4];
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      A[f] = load_frag(pa + 16 * f * ld + kb * 128);
-      B[f] = load_frag(pb + 16 * f * ld + kb * 128);
-      // tile-major scales: In rows i_base + 16 f + 4 q + v are contiguous
-      const float4 s4 = *reinterpret_cast<const float4*>(bs + kb * Nb + i_base + 16 * f + 4 * q);
-      sI[f][0] = s4.x, sI[f][1] = s4.y, sI[f][2] = s4.z, sI[f][3] = s4.w;
-      sO[f] = as[kb * Na + o_base + 16 * f + l16];
+    for (int fo = 0; fo < 4; ++fo) {
+      bo[fo] = lds_operand(st + kWgOffOut + (wo + 16 * fo) * 128, lane_lo, lane_hi);
+      so[fo] = sSO[wo + 16 * fo + l16];
     }
-    const v4f zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int fi = 0; fi < 4; ++fi)
+    for (int fi = 0; fi < 8; ++fi) {
+      const v8i ai = lds_operand(st + kWgOffIn + (wi + 16 * fi) * 128, lane_lo, lane_hi);
+      // In rows wi + 16 fi + 4q + v: four consecutive scales
+      const float4 s4 = *reinterpret_cast<const float4*>(sSI + wi + 16 * fi + 4 * q);
+      const float si[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
       for (int fo = 0; fo < 4; ++fo) {
-        const v4f p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A[fi], B[fo], zero, 0, 0, 0, 0, 0, 0);
+        const v4f p = mfma_chunk(ai, bo[fo]);
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[fi][fo][v] = __builtin_fmaf(p[v], sI[fi][v] * sO[fo], acc[fi][fo][v]);
+        for (int v = 0; v < 4; ++v) acc[fi][fo][v] = __builtin_fmaf(p[v], si[v] * so[fo], acc[fi][fo][v]);
       }
+    }
   }
+  // every load of this workgroup has landed (the last wait was vmcnt(0), or
+  // nothing was issued), so its LDS can be released after the stores
   OT* og = out + (int64_t)g * Na * Nb;
 #pragma unroll
-  for (int fo = 0; fo < 4; ++fo)
+  for (int fo = 0; fo < 4; ++fo) {
+    if (o0 + wo + 16 * fo >= Na) break;  // rows past Na: a half tile
 #pragma unroll
-    for (int fi = 0; fi < 4; ++fi) {
+    for (int fi = 0; fi < 8; ++fi) {
+      if (i0 + wi + 16 * fi >= Nb) break;
       const float v[4] = {acc[fi][fo][0], acc[fi][fo][1], acc[fi][fo][2], acc[fi][fo][3]};
-      store4(og + (o_base + 16 * fo + l16) * Nb + i_base + 16 * fi + 4 * q, v, kAcc);
+      store4(og + (int64_t)(o0 + wo + 16 * fo + l16) * Nb + i0 + wi + 16 * fi + 4 * q, v, kAcc);
     }
+  }
 }
 
 }  // namespace
@@ -353,7 +418,8 @@ extern "C" moe_status grouped_wgrad_fp8(const uint8_t* aq, const float* as, cons
               "Na=%d Nb=%d (positive multiples of 128)", Na, Nb);
   MOE_REQUIRE(G >= 1 && G <= kMaxGroups, MOE_ERR_UNSUPPORTED, "G=%d (1..%d)", G, kMaxGroups);
   MOE_REQUIRE(ld > 0 && ld % 128 == 0, MOE_ERR_SHAPE, "ld=%lld (a positive multiple of 128)", (long long)ld);
-  const int64_t n_tiles = (int64_t)G * (Na / 128) * (Nb / 128);
+  MOE_REQUIRE(ld <= (int64_t(1) << 29), MOE_ERR_UNSUPPORTED, "ld=%lld above 2^29", (long long)ld);
+  const int64_t n_tiles = (int64_t)G * ((Na + kWgTile - 1) / kWgTile) * ((Nb + kWgTile - 1) / kWgTile);
   MOE_REQUIRE(n_tiles <= 0x7fffffffLL - 8, MOE_ERR_UNSUPPORTED, "too many output tiles");
   MOE_REQUIRE(aq && as && bq && bs && padded_offsets && c, MOE_ERR_NULL, "every array is required");
   MOE_REQUIRE(aligned(aq, 16) && aligned(bq, 16) && aligned(as, 4) && aligned(bs, 4) &&
@@ -363,7 +429,7 @@ extern "C" moe_status grouped_wgrad_fp8(const uint8_t* aq, const float* as, cons
   const int64_t per_xcd = (n_tiles + 7) / 8;
   const unsigned grid = (unsigned)(8 * per_xcd);
 #define MOE_WGRAD_LAUNCH(OT, ACC)                                                                          \
-  wgrad_kernel<OT, ACC><<<grid, 256, 0, s>>>(aq, as, bq, bs, padded_offsets, Na, Nb, ld, n_tiles, per_xcd, \
+  wgrad_kernel<OT, ACC><<<grid, kWgThreads, 0, s>>>(aq, as, bq, bs, padded_offsets, Na, Nb, ld, n_tiles, per_xcd, \
                                             static_cast<OT*>(c))
   if (c_dtype == MOE_F32) {
     if (accumulate) MOE_WGRAD_LAUNCH(float, true); else MOE_WGRAD_LAUNCH(float, false);

@@ -190,7 +190,8 @@ def test_wgrad_errors():
     assert w(P, P, P, P, N0, 4, 128, 128, 256, P, 0, 0, S) == NULL
     assert w(P, P, PM, P, P, 4, 128, 128, 256, P, 0, 0, S) == ALIGN
     assert w(P, P, P, P, P, 4, 128, 128, 256, ctypes.c_void_p(0x10008), 0, 0, S) == ALIGN   # f32 c
-    assert w(P, P, P, P, P, 1024, 262144, 262144, 256, P, 0, 0, S) == UNSUP        # tile count
+    assert w(P, P, P, P, P, 1024, 524288, 524288, 256, P, 0, 0, S) == UNSUP        # tile count
+    assert w(P, P, P, P, P, 4, 128, 128, 2 ** 29 + 128, P, 0, 0, S) == UNSUP       # ld above 2^29
 
 
 def test_router_errors():
