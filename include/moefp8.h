@@ -406,8 +406,10 @@ MOE_API moe_status quant_act_128x1_grouped_e4m3(const void* x, moe_dtype x_dtype
  *           weights; an expert without rows gets zeros.  accumulate != 0
  *           adds to c's contents instead (c = c + dW in float32, then the
  *           output type's rounding).
- *  Na % 128 == Nb % 128 == 0, 1 <= G <= 1024, ld a multiple of 128.
- * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED, MOE_ERR_ALIGN
+ *  Na % 128 == Nb % 128 == 0, 1 <= G <= 1024, ld a multiple of 128 and at
+ *  most 2^29.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED (dtype, G, ld above
+ *         2^29, more than 2^31 - 8 output tiles of 256 x 256), MOE_ERR_ALIGN
  *         (aq, bq 16-byte; c 16-byte for f32, 8-byte for bf16).
  */
 MOE_API moe_status grouped_wgrad_fp8(const uint8_t* aq, const float* as, const uint8_t* bq, const float* bs,
