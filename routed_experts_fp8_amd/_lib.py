@@ -102,6 +102,9 @@ def _need(t, name, dtype, shape=None):
         raise TypeError(f"{name} must be a torch.Tensor")
     if not t.is_cuda:
         raise ValueError(f"{name} must be a device tensor")
+    if t.device.index != torch.cuda.current_device():
+        # work is enqueued on the current device's stream
+        raise ValueError(f"{name} is on {t.device}, the current device is cuda:{torch.cuda.current_device()}")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_contiguous():
@@ -115,6 +118,12 @@ def _out(out, name, shape, dtype, device):
     if out is None:
         return torch.empty(shape, dtype=dtype, device=device)
     return _need(out, name, dtype, shape)
+
+
+def _even(n, name):
+    if n % 2:
+        raise ValueError(f"{name} must be even (a gate half and an up half), got {n}")
+    return n // 2
 
 
 def _dtype_code(t):
@@ -252,7 +261,7 @@ def grouped_gemm_fp8_swiglu(aq, as_, bq, bs, offsets, hq=None, hs=None, a_row=No
     """Gate|up GEMM with fused SwiGLU + 1x128 quantisation -> (hq [M, I], hs [M, I/128]).
     a_row (int32 [M]), if given, gathers row m of A from aq[a_row[m]]."""
     M, K, G, N, A = _gemm_operands(aq, as_, bq, bs, offsets, a_row)
-    I = N // 2
+    I = _even(N, "bq rows per group (2I)")
     hq = _out(hq, "hq", (M, I), torch.uint8, aq.device)
     hs = _out(hs, "hs", (M, I // 128), torch.float32, aq.device)
     _check("grouped_gemm_fp8_swiglu", lib.grouped_gemm_fp8_swiglu(
@@ -264,7 +273,7 @@ def swiglu(gate_up, hq=None, hs=None):
     """gate_up float32 [M, 2I] -> (hq uint8 [M, I], hs float32 [M, I/128])."""
     _need(gate_up, "gate_up", torch.float32)
     M, twoI = gate_up.shape
-    I = twoI // 2
+    I = _even(twoI, "gate_up columns (2I)")
     hq = _out(hq, "hq", (M, I), torch.uint8, gate_up.device)
     hs = _out(hs, "hs", (M, I // 128), torch.float32, gate_up.device)
     _check("swiglu", lib.swiglu(_p(gate_up), M, I, _p(hq), _p(hs), _stream()))
@@ -328,7 +337,7 @@ def swiglu_backward(gate_up, dh, dq=None, ds=None, d=None):
     d (f32 [M, 2I], optional) receives [dg | du] unquantised."""
     _need(gate_up, "gate_up", torch.float32)
     M, twoI = gate_up.shape
-    I = twoI // 2
+    I = _even(twoI, "gate_up columns (2I)")
     _need(dh, "dh", torch.float32, (M, I))
     dq = _out(dq, "dq", (M, twoI), torch.uint8, gate_up.device)
     ds = _out(ds, "ds", (M, twoI // 128), torch.float32, gate_up.device)
@@ -368,7 +377,7 @@ def quant_act_128x1_grouped_e4m3(x, group_offsets, M=None, row_index=None, row_s
         raise TypeError("x must be float32 or bfloat16")
     _need(x, "x", x.dtype)
     x_rows, cols = x.shape
-    C = cols // 2 if swiglu_input else cols
+    C = _even(cols, "gate|up input columns (2C)") if swiglu_input else cols
     _need(group_offsets, "group_offsets", torch.int32)
     G = group_offsets.shape[0] - 1
     if M is None:

@@ -1,9 +1,11 @@
-"""The routed-expert FP8 MoE FFN layer forward, as a sequence of library
-calls (no host synchronisation inside).
+"""The routed-expert FP8 MoE FFN layer as sequences of library calls (no
+host synchronisation inside): weight quantisation, the forward
+(``MoEForward``), the input-side backward (``MoEBackward``) and the FP8
+weight gradients (``MoEWeightGrad``).
 
-Dataflow ([DSV3-MOE] shared + routed experts, sigmoid top-K with bias, no
-dropping; [PANGU-MOGE] grouped softmax routing; [DSV3-FP8] / [KANANA-FP8]
-fine-grained FP8):
+Forward dataflow ([DSV3-MOE] shared + routed experts, sigmoid top-K with
+bias, no dropping; [PANGU-MOGE] grouped softmax routing; [DSV3-FP8] /
+[KANANA-FP8] fine-grained FP8):
 
   quant_act_1x128_e4m3(x) -> moe_route -> moe_permute (index maps) ->
   grouped_gemm_fp8_swiglu (expert-grouped rows gathered from x's FP8 codes
@@ -16,7 +18,8 @@ tokens) runs on a side stream from the quantisation on and joins before the
 combine.
 
 Weights are quantised ahead of the forward (``quantize_weights``), as in
-training where quantisation runs once per optimizer step for all experts.
+training where quantisation runs once per optimizer step for all experts;
+the same launches can write the block-transposed copies the backward uses.
 """
 
 import torch

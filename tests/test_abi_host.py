@@ -137,6 +137,14 @@ def test_binding_requires_device_tensors():
         L.quant_act_1x128_e4m3(torch.zeros(4, 128))
 
 
+def test_binding_rejects_odd_gate_up_width():
+    """A gate|up width of 2I + 1 would pass the library's I % 128 check with
+    the wrong row stride; the binding refuses it."""
+    assert L._even(512, "gate_up columns") == 256
+    with pytest.raises(ValueError):
+        L._even(257, "gate_up columns")
+
+
 def test_backward_errors():
     c = L.lib.moe_combine_backward
     assert c(P, P, P, P, 4, 2, 100, P, P, P, N0, S) == SHAPE             # H % 128
