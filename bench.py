@@ -17,14 +17,22 @@ events recorded on the stream the library launches on, inside the timed
 region.  The CPU baseline times the oracle (test infrastructure) on a
 bounded sample of the same workload and scales it to the full layer.
 
+Besides the contract keys the line carries the per-step median and minimum
+(from per-step events), a cold-cache run (a 1 GiB buffer written before
+each step, outside the step's events, so inputs are not served from the
+L2s or the Infinity Cache) and the GPU clocks as the SMI tool reports them.
+
 usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--no-extra]
-                      [--section layer|backward]
+                      [--section layer|backward|train]
 """
 
 import argparse
 import hashlib
 import json
 import os
+import shutil
+import statistics
+import subprocess
 import sys
 import time
 
@@ -56,6 +64,65 @@ def parse():
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def gpu_clocks():
+    """Current GPU clocks as the SMI tool prints them (best effort; None if
+    no tool answers within a few seconds)."""
+    for cmd in (["amd-smi", "metric", "--clock", "--json"], ["rocm-smi", "--showclocks", "--json"]):
+        exe = shutil.which(cmd[0])
+        if exe is None:
+            continue
+        try:
+            r = subprocess.run([exe] + cmd[1:], capture_output=True, text=True, timeout=20)
+        except (OSError, subprocess.SubprocessError):
+            continue
+        if r.returncode == 0 and r.stdout.strip():
+            try:
+                return _compact_clocks(json.loads(r.stdout))
+            except ValueError:
+                return r.stdout.strip()[:2000]
+    return None
+
+
+def _compact_clocks(j):
+    """{domain: current MHz} from amd-smi's per-GPU clock records (the
+    graphics clock of every XCD, memory, fabric, ...); other layouts as
+    they came."""
+    try:
+        clk = j["gpu_data"][0]["clock"] if isinstance(j, dict) else j[0]["clock"]
+        return {k: v["clk"]["value"] for k, v in clk.items()
+                if isinstance(v, dict) and isinstance(v.get("clk"), dict) and "value" in v["clk"]}
+    except (KeyError, IndexError, TypeError):
+        return j
+
+
+def cold_steps(step, n, torch):
+    """Median and minimum of n single steps, each after writing a 1 GiB
+    buffer (outside the step's events): the inputs then come from HBM, not
+    from the L2s or the 256 MB Infinity Cache."""
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    times = []
+    for i in range(n):
+        flush.fill_(float(i))
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        step()
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    del flush
+    return dict(steps=n, median_ms=statistics.median(times), min_ms=min(times), flush_bytes=1 << 30)
+
+
+def copy_rate(torch, nbytes=1 << 30, reps=10):
+    """A plain device copy (torch's copy kernel) of nbytes: read + write
+    bytes per second, the box's measured streaming ceiling beside 8 TB/s."""
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    ms = time_op(lambda: b.copy_(a), reps, torch)
+    del a, b
+    return dict(copy_bytes=nbytes, ms=ms, GBps=2 * nbytes / ms / 1e6)
 
 
 def gemm1_bytes(T, K, H, E, I):
@@ -196,14 +263,30 @@ def router_rows(cfg, d, fwd, torch, R, synth, reps=5):
 
 def graph_rows(torch, R, synth, reps=50):
     """The layer forward eager vs replayed from a captured HIP graph on the
-    small shared-expert layer (T=200, H=512, 16 experts top-4), where kernel
-    launches, not the kernels, set the step time."""
+    small layers, where kernel launches, not the kernels, set the step time:
+    the tiny workload (T=256, H=512, 8 experts, top-2 softmax) and a small
+    shared-expert layer (T=200, H=512, 16 experts top-4 + shared, whose
+    capture holds the side stream's fork and join)."""
+    tiny = synth.get_config("tiny")
+    shared = dict(tiny, T=200, E=16, K=4, I=256, shared_I=256, bias_std=0.01,
+                  route=dict(mode="sigmoid_bias", K=4, normalize=True), x_dtype="bf16", w_dtype="bf16")
+    out = {}
+    for key, cfg, label in (("tiny", tiny, tiny["name"]),
+                            ("shared_layer", shared, "T=200, H=512, 16 experts top-4 + shared")):
+        r = graph_row(cfg, torch, R, synth, reps)
+        r["workload"] = label
+        r["eager_tokens_per_s"] = cfg["T"] / (r["eager_ms"] / 1e3)
+        r["graph_tokens_per_s"] = cfg["T"] / (r["graph_replay_ms"] / 1e3)
+        out[key] = r
+    return out
+
+
+def graph_row(cfg, torch, R, synth, reps):
     dev = torch.device("cuda:0")
-    cfg = dict(synth.get_config("tiny"), T=200, E=16, K=4, I=256, shared_I=256, bias_std=0.01,
-               route=dict(mode="sigmoid_bias", K=4, normalize=True), x_dtype="bf16", w_dtype="bf16")
     d = synth.layer_inputs(cfg, dev, seed=0)
-    w = R.quantize_weights(d["w13"], d["w2"], d["sw13"], d["sw2"])
-    fwd = R.MoEForward(cfg["T"], cfg["H"], cfg["E"], cfg["I"], cfg["route"], w, dev, shared_I=cfg["shared_I"])
+    w = R.quantize_weights(d["w13"], d["w2"], d.get("sw13"), d.get("sw2"))
+    fwd = R.MoEForward(cfg["T"], cfg["H"], cfg["E"], cfg["I"], cfg["route"], w, dev,
+                       shared_I=cfg.get("shared_I"))
     eager = time_op(lambda: fwd(d["x"], d["logits"], d["bias"]), reps, torch)
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -215,7 +298,7 @@ def graph_rows(torch, R, synth, reps=50):
     with torch.cuda.graph(g):
         fwd(d["x"], d["logits"], d["bias"])
     graph = time_op(g.replay, reps, torch)
-    return dict(workload="T=200, H=512, 16 experts top-4 + shared", eager_ms=eager, graph_replay_ms=graph)
+    return dict(eager_ms=eager, graph_replay_ms=graph)
 
 
 def backward_rows(cfg, d, w, torch, R, synth, reps=5):
@@ -534,6 +617,9 @@ def main():
     for _ in range(args.warmup):
         fwd(d["x"], d["logits"], d["bias"])
     torch.cuda.synchronize()
+    log("cold-cache steps")
+    cold = cold_steps(lambda: fwd(d["x"], d["logits"], d["bias"]), 10, torch)
+    torch.cuda.synchronize()
 
     log(f"timing {args.steps} steps")
     marks = []
@@ -557,6 +643,8 @@ def main():
     torch.cuda.synchronize()
     wall_ms = (time.perf_counter() - t0) * 1e3 / args.steps
     ms_per_step = start.elapsed_time(end) / args.steps
+    step_ms = [marks[i][0][1].elapsed_time(marks[i + 1][0][1]) for i in range(len(marks) - 1)]
+    step_ms.append(marks[-1][0][1].elapsed_time(end))
     stage_ms = {}
     for step in marks:
         for (_, a), (name, b) in zip(step[:-1], step[1:]):
@@ -614,6 +702,8 @@ def main():
         extra["graph"] = graph_rows(torch, R, synth)
         log("other workloads: MoGE and skewed-load layers")
         extra["other_workloads"] = other_workload_rows(torch, R, synth)
+        log("measured streaming ceiling: a plain 1 GiB device copy")
+        extra["measured_copy"] = copy_rate(torch)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle, bounded sample)")
@@ -627,7 +717,10 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "ms_per_step_median": statistics.median(step_ms),
+        "ms_per_step_min": min(step_ms),
         "wall_ms_per_step": wall_ms,
+        "cold_cache": cold,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -641,6 +734,7 @@ def main():
         "cpu_baseline": cpu,
         "stages_ms": stage_ms,
         "gemm": gemm,
+        "gpu": {"name": torch.cuda.get_device_name(0), "clocks": gpu_clocks()},
         "extra": extra,
     }
     print(json.dumps(line), flush=True)
