@@ -98,7 +98,8 @@ def test_gemm_errors():
     f = L.lib.grouped_gemm_fp8_blockscaled
     assert f(P, P, N0, 0, P, P, P, 4, 64, 100, 128, P, 0, S) == SHAPE
     assert f(P, P, N0, 0, P, P, P, 4, 64, 128, 130, P, 0, S) == SHAPE
-    assert f(P, P, N0, 0, P, P, P, 2048, 64, 128, 128, P, 0, S) == UNSUP
+    assert f(P, P, N0, 0, P, P, P, 2048, 64, 128, 128, P, 0, S) == UNSUP            # G > 1024
+    assert f(P, P, N0, 0, P, P, P, 4, 64, 128, 65536 + 128, P, 0, S) == UNSUP       # K > 65536
     assert f(P, P, N0, 0, P, P, P, 0, 64, 128, 128, P, 0, S) == SHAPE
     assert f(P, P, N0, 0, P, P, N0, 4, 64, 128, 128, P, 0, S) == NULL
     assert f(P, P, N0, 0, P, P, P, 4, 64, 128, 128, N0, 0, S) == NULL

@@ -345,6 +345,37 @@ def test_grouped_gemm_row_gather(K):
         assert torch.equal(hq, hq2) and torch.equal(hs, hs2)
 
 
+def _random_problem(sizes, N, K, rng):
+    """Random codes and scales (the GEMM's contract takes any)."""
+    G, M = len(sizes), int(sum(sizes))
+    aq, bq = _random_codes(rng, (M, K)), _random_codes(rng, (G, N, K))
+    as_ = rng.uniform(0.5, 2.0, (M, K // 128)).astype(np.float32)
+    bs = rng.uniform(0.5, 2.0, (G, N // 128, K // 128)).astype(np.float32)
+    return aq, as_, bq, bs, rand_offsets(rng, sizes)
+
+
+def test_grouped_gemm_at_the_limits():
+    """The two size limits of the grouped GEMM: 1024 groups (every
+    workgroup's tile table then scans 1024 group offsets, two per thread),
+    mostly empty or 1-3 rows with a few long and ragged ones; and K = 65536
+    (512 chunks, one tile per workgroup).  Both against the oracle, the
+    fused SwiGLU against the unfused GEMM + standalone SwiGLU."""
+    sizes = list(RNG.integers(0, 4, 1024))
+    sizes[7], sizes[500], sizes[1023] = 161, 300, 17
+    aq, as_, bq, bs, off = _random_problem(sizes, 256, 256, RNG)
+    args = [to_dev(v) for v in (aq, as_, bq, bs, off)]
+    c = R.grouped_gemm_fp8_blockscaled(*args)
+    C, Mag = O.grouped_gemm(aq, as_, bq, bs, off)
+    assert_gemm_close(np_(c), C, Mag)
+    hq, hs = R.grouped_gemm_fp8_swiglu(*args)
+    hq2, hs2 = R.swiglu(c)
+    assert torch.equal(hq, hq2) and torch.equal(hs, hs2)
+    aq, as_, bq, bs, off = _random_problem([3, 0, 17], 128, 65536, RNG)
+    c = R.grouped_gemm_fp8_blockscaled(*[to_dev(v) for v in (aq, as_, bq, bs, off)])
+    C, Mag = O.grouped_gemm(aq, as_, bq, bs, off)
+    assert_gemm_close(np_(c), C, Mag)
+
+
 def test_grouped_gemm_exact_integers():
     """Integer codes with unit scales: every partial sum is an integer below
     2^24, so the float32 result must equal the exact integer product."""
