@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 RNG = np.random.default_rng(23)
 
 
-@pytest.mark.parametrize("T,K,H", [(1, 1, 128), (37, 4, 512), (200, 8, 1024)])
+@pytest.mark.parametrize("T,K,H", [(1, 1, 128), (37, 4, 512), (200, 8, 1024), (60, 16, 256)])   # K = 16: the limit
 def test_combine_backward(T, K, H):
     y = RNG.standard_normal((T * K, H)).astype(np.float32)
     y[::5] *= np.float32(1e-3)
@@ -61,9 +61,9 @@ def _route_inputs(T, E, mode, **kw):
     return logits, lt, idx_g, idx_o, gate_o
 
 
-@pytest.mark.parametrize("normalize", [True, False])
-def test_route_backward_sigmoid(normalize):
-    T, E, K = 300, 256, 8
+@pytest.mark.parametrize("normalize,T,E,K", [(True, 300, 256, 8), (False, 300, 256, 8),
+                                              (True, 40, 256, 64)])          # K = 64: the limit
+def test_route_backward_sigmoid(normalize, T, E, K):
     logits, lt, idx_g, idx_o, gate_o = _route_inputs(T, E, "sigmoid_bias", K=K, normalize=normalize)
     dg = RNG.standard_normal((T, K)).astype(np.float32)
     d = np_(R.moe_route_backward(lt, idx_g, to_dev(dg), "sigmoid_bias", normalize=normalize))
@@ -72,7 +72,7 @@ def test_route_backward_sigmoid(normalize):
     assert np.all(np.abs(d - ref) <= np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64) + 1e-37)
 
 
-@pytest.mark.parametrize("T,E,G,Kp", [(300, 64, 8, 1), (50, 16, 1, 2)])
+@pytest.mark.parametrize("T,E,G,Kp", [(300, 64, 8, 1), (50, 16, 1, 2), (40, 128, 8, 8)])   # K = 64: the limit
 def test_route_backward_softmax(T, E, G, Kp):
     logits, lt, idx_g, idx_o, gate_o = _route_inputs(T, E, "softmax_grouped", G=G, Kp=Kp)
     dg = RNG.standard_normal((T, G * Kp)).astype(np.float32)
