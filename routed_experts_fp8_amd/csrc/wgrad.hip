@@ -42,10 +42,10 @@
 //   consecutive input features of one output row and stores them as one
 //   16-byte (float32) or 8-byte (bf16) vector.  Tiles of one expert are
 //   consecutive and the logical tile order is dealt XCD by XCD; inside an
-//   expert the order is blocked (4 output-feature tiles by every
+//   expert the order is blocked (2 output-feature tiles by every
 //   input-feature tile), so the tiles in flight on one XCD share a few
 //   operand slabs, which stay in its L2 despite the output stream passing
-//   through it.  One tile per workgroup: a persistent walk would have to
+//   through it, and write long contiguous runs of the same output rows.  One tile per workgroup: a persistent walk would have to
 //   wait for the next tile's loads behind the previous tile's stores (one
 //   vector-memory counter counts both).
 #include "host_common.h"
@@ -55,7 +55,7 @@ namespace moefp8 {
 namespace {
 
 constexpr int kMaxGroups = 1024;
-constexpr int kOB = 4;  // output-feature tiles per block of the wgrad tile order
+constexpr int kOB = 2;  // output-feature tiles per block of the wgrad tile order (measured: 1, 2, 4, 8)
 
 // wgrad_kernel: 256 x 256 output tiles, 8 waves, a 2-stage LDS ring
 constexpr int kWgThreads = 512;
