@@ -120,8 +120,12 @@ __global__ __launch_bounds__(256) void quant128x1_kernel(
     const float* __restrict__ row_scale, const int* __restrict__ offsets, const int* __restrict__ poff, int G,
     int64_t M, int64_t ld, uint8_t* __restrict__ qt, float* __restrict__ st) {
   __shared__ float tile[64][132];
-  const int tt = blockIdx.x;
-  const int cb = blockIdx.y;
+  // column blocks fastest: consecutive workgroups read adjacent 128-byte
+  // pieces of the same source rows (measured 5-10 % faster than row tiles
+  // fastest, whose writes are the contiguous ones)
+  const int ncb = C / 64;
+  const int tt = (int)(blockIdx.x / ncb);
+  const int cb = (int)(blockIdx.x % ncb);
   const int64_t prow = (int64_t)tt * 128;
   if (prow >= poff[G] || prow + 128 > ld) return;  // past the last expert's tiles (uniform)
   // expert g: the largest g with P_g <= prow (empty experts have P_g == P_{g+1})
@@ -385,10 +389,12 @@ extern "C" moe_status quant_act_128x1_grouped_e4m3(const void* x, moe_dtype x_dt
   MOE_REQUIRE(aligned(group_offsets, 4) && aligned(padded_offsets, 4) && aligned(x, 16) && aligned(qt, 16) &&
                   aligned(st, 4) && aligned(row_index, 4) && aligned(row_scale, 4),
               MOE_ERR_ALIGN, "x and qt need 16-byte alignment, the others 4-byte");
+  const int64_t blocks = ((M + 127) / 128 + G) * (int64_t)(C / 64);
+  MOE_REQUIRE(blocks <= 0x7fffffffLL, MOE_ERR_UNSUPPORTED, "too many (128-row tile, 64-column) blocks");
   hipStream_t s = as_stream(stream);
   padded_offsets_kernel<<<1, 256, 0, s>>>(group_offsets, G, padded_offsets);
   if (M > 0) {
-    const dim3 grid((unsigned)((M + 127) / 128 + G), (unsigned)(C / 64));
+    const dim3 grid((unsigned)blocks);
     const int64_t ldx = swiglu_input ? 2 * (int64_t)C : C;
     if (x_dtype == MOE_F32) {
       if (swiglu_input)

@@ -190,6 +190,7 @@ def test_wgrad_errors():
     assert q(N0, 0, 0, 300, 128, N0, N0, P, 4, 300, 896, P, P, P, S) == NULL      # x
     assert q(PM, 0, 0, 300, 128, N0, N0, P, 4, 300, 896, P, P, P, S) == ALIGN
     assert q(P, 0, 0, 300, 128, N0, N0, P, 4, 300, 896, P, PM, P, S) == ALIGN     # qt
+    assert q(P, 0, 0, 1 << 20, 1 << 30, N0, N0, P, 4, 1 << 20, (1 << 20) + 512, P, P, P, S) == UNSUP   # blocks
     w = L.lib.grouped_wgrad_fp8
     #     aq as bq bs poff G  Na   Nb   ld   c dt acc
     assert w(P, P, P, P, P, 4, 100, 128, 256, P, 0, 0, S) == SHAPE
