@@ -591,8 +591,8 @@ def train_section(args, cfg, d, torch, R, synth):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only; --gpus {args.gpus} is not supported "
-              "(the expert-parallel multi-GPU path is not part of it)", file=sys.stderr)
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the expert-parallel multi-GPU path is not implemented)", file=sys.stderr)
         sys.exit(2)
     import torch
     import routed_experts_fp8_amd as R
