@@ -117,7 +117,7 @@ def cold_steps(step, n, torch):
 
 def copy_rate(torch, nbytes=1 << 30, reps=10):
     """A plain device copy (torch's copy kernel) of nbytes: read + write
-    bytes per second, the box's measured streaming ceiling beside 8 TB/s."""
+    bytes per second, the device's measured streaming ceiling beside 8 TB/s."""
     a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
     ms = time_op(lambda: b.copy_(a), reps, torch)
