@@ -98,13 +98,18 @@ def _scales_dev(s, ld):
     return to_dev(np.ascontiguousarray(_pad_ld(s, ld // 128).T))
 
 
-@pytest.mark.parametrize("sizes,Na,Nb", [([0, 5, 300, 128, 1], 256, 384), ([700], 128, 128),
-                                         ([0, 0, 0], 128, 256)])
-def test_wgrad_gemm(sizes, Na, Nb):
+@pytest.mark.parametrize("sizes,Na,Nb,extra_ld", [([0, 5, 300, 128, 1], 256, 384, 0), ([700], 128, 128, 0),
+                                                  ([0, 0, 0], 128, 256, 0), ([9, 140], 384, 256, 384)])
+def test_wgrad_gemm(sizes, Na, Nb, extra_ld):
+    """extra_ld: a row stride beyond the smallest admissible one (columns
+    past the last expert's padded rows are never read)."""
     aq, as_, bq, bs, p = _wgrad_problem(sizes, Na, Nb)
     C, Mag = O.wgrad_gemm(aq, as_, bq, bs, p)
-    ld = R.moe_wgrad_padded_rows(sum(sizes), len(sizes))
-    args = [to_dev(_pad_ld(aq, ld)), _scales_dev(as_, ld), to_dev(_pad_ld(bq, ld)), _scales_dev(bs, ld), to_dev(p)]
+    ld = R.moe_wgrad_padded_rows(sum(sizes), len(sizes)) + extra_ld
+    aqp, bqp = _pad_ld(aq, ld), _pad_ld(bq, ld)
+    aqp[:, int(p[-1]):] = 0x38                     # code 1.0 past the last expert: must not be read
+    bqp[:, int(p[-1]):] = 0x38
+    args = [to_dev(aqp), _scales_dev(as_, ld), to_dev(bqp), _scales_dev(bs, ld), to_dev(p)]
     c = R.grouped_wgrad_fp8(*args)
     cg = np_(c).astype(np.float64)
     assert np.all(np.abs(cg - C) <= GEMM_RTOL * Mag + 1e-30)
