@@ -125,6 +125,24 @@ def copy_rate(torch, nbytes=1 << 30, reps=10):
     return dict(copy_bytes=nbytes, ms=ms, GBps=2 * nbytes / ms / 1e6)
 
 
+def dense_fp8_gemm_rate(torch, n=8192, reps=20):
+    """A plain dense FP8 GEMM from the vendor library (torch._scaled_mm, one
+    scale per tensor) at n x n x n: the device's measured matrix-core rate
+    for FP8 beside the 5.0 PFLOP/s datasheet figure.  Context only; the
+    layer's GEMMs are the library's own kernels (block scales need the
+    per-chunk promotion)."""
+    try:
+        a = torch.randn(n, n, device="cuda").to(torch.float8_e4m3fn)
+        b = torch.randn(n, n, device="cuda").to(torch.float8_e4m3fn)
+        one = torch.tensor(1.0, device="cuda")
+        ms = time_op(lambda: torch._scaled_mm(a, b.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16),
+                     reps, torch)
+    except (RuntimeError, AttributeError, TypeError) as ex:
+        return dict(error=repr(ex)[:200])
+    return dict(m=n, n=n, k=n, ms=ms, TFLOPs=2 * n ** 3 / ms / 1e9,
+                frac_mfma=2 * n ** 3 / ms / 1e9 / FP8_PEAK_TFLOPS)
+
+
 def gemm1_bytes(T, K, H, E, I):
     """Algorithmic HBM bytes of the fused gate|up launch: activation codes and
     scales, every expert's gate|up codes and block scales, h codes and scales."""
@@ -704,6 +722,8 @@ def main():
         extra["other_workloads"] = other_workload_rows(torch, R, synth)
         log("measured streaming ceiling: a plain 1 GiB device copy")
         extra["measured_copy"] = copy_rate(torch)
+        log("measured FP8 matrix rate: a dense vendor-library FP8 GEMM")
+        extra["measured_dense_fp8_gemm"] = dense_fp8_gemm_rate(torch)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle, bounded sample)")
