@@ -191,3 +191,56 @@ def test_layer_forward_in_a_hip_graph():
     g.replay()
     torch.cuda.synchronize()
     assert np.array_equal(bf16_bits(y_graph), ref2)
+
+
+def test_training_step_in_a_hip_graph():
+    """A whole training step of the layer (forward keeping its gate|up
+    output, input-side backward, FP8 weight gradients, balancing bias
+    update) captured once and replayed: nothing in it allocates or clears
+    memory, its side-stream work joins the capturing stream, so every
+    replay (with eager steps in between, the bias reset before each) gives
+    the eager step's results bit for bit."""
+    cfg = _variant("tiny_sigmoid_shared")
+    T, H, E, I = cfg["T"], cfg["H"], cfg["E"], cfg["I"]
+    d = synth.layer_inputs(cfg, dev(), seed=0)
+    w, wt = R.quantize_weights(d["w13"], d["w2"], d.get("sw13"), d.get("sw2"), transposed=True)
+    fwd = R.MoEForward(T, H, E, I, cfg["route"], w, dev(), fused=False, shared_I=cfg.get("shared_I"))
+    bwd = R.MoEBackward(fwd, wt, weight_grad=True)
+    wg = R.MoEWeightGrad(bwd)
+    x, logits, bias0 = d["x"].clone(), d["logits"].clone(), d["bias"].clone()
+    dy = synth.output_grad(T, H, dev(), seed=4)
+    bias = bias0.clone()
+
+    def step():
+        y = fwd(x, logits, bias)
+        dx, dl = bwd(dy, logits)
+        grads = wg(x, dy)
+        fwd.update_bias(bias, 1e-3)
+        return [y, dx, dl, bias] + [grads[k] for k in sorted(grads)]
+
+    def snapshot(outs):
+        return [o.clone() for o in outs]
+
+    ref = snapshot(step())
+    torch.cuda.synchronize()
+    assert not torch.equal(ref[3], bias0)               # the update moved the bias
+    bias.copy_(bias0)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):                          # warm-up on the capture stream
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    bias.copy_(bias0)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        outs = step()
+    for _ in range(3):
+        bias.copy_(bias0)
+        g.replay()
+        torch.cuda.synchronize()
+        for o, r in zip(outs, ref):
+            assert torch.equal(o.view(torch.uint8), r.view(torch.uint8))
+        bias.copy_(bias0)
+        step()                                          # eager work between replays
+        torch.cuda.synchronize()
