@@ -143,6 +143,17 @@ def dense_fp8_gemm_rate(torch, n=8192, reps=20):
                 frac_mfma=2 * n ** 3 / ms / 1e9 / FP8_PEAK_TFLOPS)
 
 
+def wgrad_bytes(E, H, I, wg):
+    """Algorithmic bytes of the down and gate|up weight-gradient launches:
+    float32 gradients written once, the two 128x1 operands read once over
+    the padded rows the experts own (P_E, from the last call), and their
+    tile scales."""
+    pg = int(wg.buf["poff"][-1].item())
+    b2 = 4 * E * H * I + (H + I) * pg + 4 * (H + I) * (pg // 128)
+    b13 = 4 * E * 2 * I * H + (2 * I + H) * pg + 4 * (2 * I + H) * (pg // 128)
+    return b2, b13
+
+
 def gemm1_bytes(T, K, H, E, I):
     """Algorithmic HBM bytes of the fused gate|up launch: activation codes and
     scales, every expert's gate|up codes and block scales, h codes and scales."""
@@ -350,8 +361,7 @@ def backward_rows(cfg, d, w, torch, R, synth, reps=5):
     wg = R.MoEWeightGrad(bwd)
     total_w, st_w = staged(lambda mark: wg(d["x"], dy, on_stage=mark), reps, torch)
     ld = wg.ld
-    b2 = 4 * E * H * I + (H + I) * ld + 4 * (H + I) * (ld // 128)
-    b13 = 4 * E * 2 * I * H + (2 * I + H) * ld + 4 * (2 * I + H) * (ld // 128)
+    b2, b13 = wgrad_bytes(E, H, I, wg)
     rows = {}
     for name, stage, nbytes, fl in (("down_wgrad", "down_wgrad", b2, gemm_flops(M, H, I)),
                                     ("gate_up_wgrad", "gate_up_wgrad", b13, gemm_flops(M, 2 * I, H))):
@@ -587,22 +597,36 @@ def train_section(args, cfg, d, torch, R, synth):
         m("quantize_and_transpose_weights")
         fwd(d["x"], d["logits"], bias)
         m("forward")
-        bwd(dy, d["logits"])
-        m("backward")
-        wg(d["x"], dy)
-        m("weight_gradients")
+        bwd(dy, d["logits"], on_stage=mark)     # its own stages
+        wg(d["x"], dy, on_stage=mark)
         fwd.update_bias(bias, 1e-3)
         m("bias_update")
 
     for _ in range(args.warmup):
         step(None)
     torch.cuda.synchronize()
-    total, st = staged(step, args.steps, torch)
+    total, detail = staged(step, args.steps, torch)
+    bwd_keys = ("combine_backward", "down_dgrad", "swiglu_backward", "gate_up_dgrad", "shared_join",
+                "unpermute_sum", "route_backward")
+    wg_keys = ("quant_down_operands", "down_wgrad", "quant_gate_up_operands", "gate_up_wgrad", "shared_wgrad")
+    st = {"quantize_and_transpose_weights": detail["quantize_and_transpose_weights"],
+          "forward": detail["forward"],
+          "backward": sum(detail.get(k, 0.0) for k in bwd_keys),
+          "weight_gradients": sum(detail.get(k, 0.0) for k in wg_keys),
+          "bias_update": detail["bias_update"]}
+    # the step's longest single launch: the routed gate|up weight gradient
+    _, b13 = wgrad_bytes(E, H, I, wg)
+    ms_w = detail["gate_up_wgrad"]
+    roofline = dict(bound="hbm", achieved=b13 / ms_w / 1e6, peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=b13 / ms_w / 1e6 / HBM_PEAK_GBS, traffic=None,
+                    kernel="grouped_wgrad_fp8 (routed gate|up weight gradient, float32)",
+                    algorithmic_bytes_per_launch=b13)
     cpu = None if args.no_cpu_baseline else cpu_baseline_train(cfg, d, dy)
     line = {"metric": "MoE-layer training step (FP8 weights, forward, backward, FP8 weight gradients), tokens/s, 1 GPU",
             "value": T / (total / 1e3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
             "warmup": args.warmup, "ms_per_step": total, "higher_is_better": True, "dtype": "fp8_e4m3",
-            "data": "synthetic", "config": {"workload": cfg["name"]}, "stages_ms": st, "cpu_baseline": cpu}
+            "data": "synthetic", "config": {"workload": cfg["name"]}, "stages_ms": st,
+            "stages_detail_ms": detail, "roofline": roofline, "cpu_baseline": cpu}
     print(json.dumps(line), flush=True)
 
 
