@@ -385,7 +385,8 @@ MOE_API moe_status moe_wgrad_padded_rows(int64_t M, int32_t G, int64_t* rows);
  *               column c at st[j, c], for the tiles below P_G)
  *  C % 128 == 0, 1 <= G <= 1024.
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (C, ld, x_rows), MOE_ERR_UNSUPPORTED
- *         (dtype, G, a bf16 gate|up input), MOE_ERR_ALIGN (x, qt 16-byte).
+ *         (dtype, G, a bf16 gate|up input, more than 2^31 - 1 blocks of 128
+ *         rows x 64 columns), MOE_ERR_ALIGN (x, qt 16-byte).
  */
 MOE_API moe_status quant_act_128x1_grouped_e4m3(const void* x, moe_dtype x_dtype, int32_t swiglu_input,
                                         int64_t x_rows, int32_t C, const int32_t* row_index,
