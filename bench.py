@@ -170,14 +170,15 @@ def source_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic(name, kernel_src):
+def measured_traffic(name, kernel_src, workload):
     """HBM traffic measured by rocprofv3 counters for this kernel, if the
-    committed measurement was taken on the current kernel source."""
+    committed measurement was taken on the current kernel source and on the
+    workload being timed."""
     f = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
     if not os.path.exists(f):
         return None
     rec = json.load(open(f))
-    if rec.get("kernel_source_sha256_16") != source_hash(kernel_src):
+    if rec.get("kernel_source_sha256_16") != source_hash(kernel_src) or rec.get("workload") != workload:
         return None
     return rec.get("bytes_per_launch")
 
@@ -727,7 +728,7 @@ def main():
                                      frac_mfma=all_gemm_flops / all_gemm_ms / 1e9 / FP8_PEAK_TFLOPS)
 
     traffic = measured_traffic("gemm1_swiglu_dsv3", os.path.join(ROOT, "routed_experts_fp8_amd", "csrc",
-                                                                  "gemm.hip"))
+                                                                  "gemm.hip"), cfg["name"])
     roofline = dict(bound="hbm", achieved=g1_gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=g1_gbs / HBM_PEAK_GBS,
                     traffic=traffic, kernel="grouped_gemm_fp8_swiglu (routed gate|up GEMM + SwiGLU + quant)",
                     algorithmic_bytes_per_launch=g1_bytes)
