@@ -424,12 +424,17 @@ def cpu_baseline(cfg, d, n_experts=12, shared_tokens=1024, combine_tokens=2048):
     import oracle as O
     from threadpoolctl import threadpool_info
     T, H, E, I, K = cfg["T"], cfg["H"], cfg["E"], cfg["I"], cfg["K"]
+    shared_tokens, combine_tokens = min(shared_tokens, T), min(combine_tokens, T)
     x = d["x"].float().cpu().numpy()
     logits = d["logits"].cpu().numpy()
     bias = d["bias"].cpu().numpy() if d["bias"] is not None else None
     t = {}
+    rc = cfg["route"]
     t0 = time.perf_counter()
-    idx, gate = O.route_sigmoid_bias(logits, bias, K, True)
+    if rc["mode"] == "sigmoid_bias":
+        idx, gate = O.route_sigmoid_bias(logits, bias, K, rc.get("normalize", True))
+    else:
+        idx, gate = O.route_softmax_grouped(logits, rc["n_groups"], rc["k_per_group"])
     t["route"] = time.perf_counter() - t0
     t0 = time.perf_counter()
     xq, xs = O.quant_act_1x128(x)
@@ -453,14 +458,16 @@ def cpu_baseline(cfg, d, n_experts=12, shared_tokens=1024, combine_tokens=2048):
         O.grouped_gemm(hq, hs, w2q, w2s, off, with_mag=False)
         t_exp += time.perf_counter() - t0
         rows_done += int(r1 - r0)
-    sw13q, sw13s = O.quant_weight_128x128(d["sw13"].float().cpu().numpy())
-    sw2q, sw2s = O.quant_weight_128x128(d["sw2"].float().cpu().numpy())
-    off = np.array([0, shared_tokens], np.int32)
-    t0 = time.perf_counter()
-    c1, _ = O.grouped_gemm(xq[:shared_tokens], xs[:shared_tokens], sw13q, sw13s, off, with_mag=False)
-    hq, hs, _ = O.swiglu_quant(c1.astype(np.float32))
-    O.grouped_gemm(hq, hs, sw2q, sw2s, off, with_mag=False)
-    t_sh = time.perf_counter() - t0
+    t_sh = 0.0
+    if cfg.get("shared_I"):
+        sw13q, sw13s = O.quant_weight_128x128(d["sw13"].float().cpu().numpy())
+        sw2q, sw2s = O.quant_weight_128x128(d["sw2"].float().cpu().numpy())
+        off = np.array([0, shared_tokens], np.int32)
+        t0 = time.perf_counter()
+        c1, _ = O.grouped_gemm(xq[:shared_tokens], xs[:shared_tokens], sw13q, sw13s, off, with_mag=False)
+        hq, hs, _ = O.swiglu_quant(c1.astype(np.float32))
+        O.grouped_gemm(hq, hs, sw2q, sw2s, off, with_mag=False)
+        t_sh = time.perf_counter() - t0
     yperm = np.zeros((combine_tokens * K, H))
     dst = np.arange(combine_tokens * K).reshape(combine_tokens, K)
     t0 = time.perf_counter()
@@ -473,8 +480,9 @@ def cpu_baseline(cfg, d, n_experts=12, shared_tokens=1024, combine_tokens=2048):
     return dict(value=T / total, unit="tokens/s", cores=threads, kind="oracle",
                 sample=(f"oracle layer forward on the {cfg['name']} workload: routing, activation "
                         f"quantisation and permutation of all {T} tokens; routed-expert FFN for "
-                        f"{n_experts} median-load experts ({rows_done} of {T * K} rows, scaled by rows); "
-                        f"shared expert for {shared_tokens} tokens and combine for {combine_tokens} "
+                        f"{len(experts)} median-load experts ({rows_done} of {T * K} rows, scaled by rows); "
+                        + (f"shared expert for {shared_tokens} tokens and " if cfg.get("shared_I") else "")
+                        + f"combine for {combine_tokens} "
                         f"tokens (scaled by tokens); {sampled:.1f} s of CPU work measured, "
                         f"{total:.1f} s estimated for the full layer"),
                 seconds_full_layer_estimate=total)
