@@ -737,9 +737,18 @@ def main():
 
     traffic = measured_traffic("gemm1_swiglu_dsv3", os.path.join(ROOT, "routed_experts_fp8_amd", "csrc",
                                                                   "gemm.hip"), cfg["name"])
-    roofline = dict(bound="hbm", achieved=g1_gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=g1_gbs / HBM_PEAK_GBS,
-                    traffic=traffic, kernel="grouped_gemm_fp8_swiglu (routed gate|up GEMM + SwiGLU + quant)",
-                    algorithmic_bytes_per_launch=g1_bytes)
+    # the launch's bound from its arithmetic intensity: HBM below the ridge
+    # point (peak flop/s over peak bytes/s = 625 flop/B), the FP8 matrix
+    # cores above it (the compute-bound MoGE and skewed-load shapes)
+    kernel = "grouped_gemm_fp8_swiglu (routed gate|up GEMM + SwiGLU + quant)"
+    if g1_flops / g1_bytes <= FP8_PEAK_TFLOPS * 1e3 / HBM_PEAK_GBS:
+        roofline = dict(bound="hbm", achieved=g1_gbs, peak=HBM_PEAK_GBS, unit="GB/s", frac=g1_gbs / HBM_PEAK_GBS,
+                        traffic=traffic, kernel=kernel, algorithmic_bytes_per_launch=g1_bytes)
+    else:
+        g1_tf = g1_flops / g1_ms / 1e9
+        roofline = dict(bound="mfma", achieved=g1_tf, peak=FP8_PEAK_TFLOPS, unit="TFLOP/s",
+                        frac=g1_tf / FP8_PEAK_TFLOPS, traffic=traffic, kernel=kernel,
+                        algorithmic_flops_per_launch=g1_flops, algorithmic_bytes_per_launch=g1_bytes)
 
     extra = None
     if not args.no_extra:
