@@ -216,3 +216,25 @@ def test_router_errors():
     assert b(P, 0, 0.1, P, S) == SHAPE
     assert b(N0, 8, 0.1, P, S) == NULL
     assert b(P, 8, 0.1, ctypes.c_void_p(0x10002), S) == ALIGN
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built library the binding raises instead of falling back."""
+    monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "libmoefp8.so"))
+    with pytest.raises(ImportError):
+        L._load()
+
+
+def test_product_path_does_not_use_the_oracle():
+    """No module of the package imports or names the oracle (test
+    infrastructure only): the computation has no CPU path."""
+    import ast
+    import pathlib
+    pkg = pathlib.Path(L.__file__).parent
+    for f in pkg.glob("*.py"):
+        tree = ast.parse(f.read_text())
+        for node in ast.walk(tree):
+            if isinstance(node, ast.Import):
+                assert not any(a.name.split(".")[0] == "oracle" for a in node.names), f
+            if isinstance(node, ast.ImportFrom):
+                assert (node.module or "").split(".")[0] != "oracle", f
