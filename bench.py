@@ -30,9 +30,8 @@ import argparse
 import hashlib
 import json
 import os
-import shutil
+import re
 import statistics
-import subprocess
 import sys
 import time
 
@@ -67,34 +66,27 @@ def log(*a):
 
 
 def gpu_clocks():
-    """Current GPU clocks as the SMI tool prints them (best effort; None if
-    no tool answers within a few seconds)."""
-    for cmd in (["amd-smi", "metric", "--clock", "--json"], ["rocm-smi", "--showclocks", "--json"]):
-        exe = shutil.which(cmd[0])
-        if exe is None:
-            continue
-        try:
-            r = subprocess.run([exe] + cmd[1:], capture_output=True, text=True, timeout=20)
-        except (OSError, subprocess.SubprocessError):
-            continue
-        if r.returncode == 0 and r.stdout.strip():
+    """Current GPU clocks read from the driver's sysfs tables (no child
+    process: under a profiler that preloads itself, a spawned tool would be
+    an exec from a process that has set up the GPU).  {domain: MHz} of the
+    level marked current in pp_dpm_sclk / pp_dpm_mclk / pp_dpm_fclk of the
+    first card that has them, or None."""
+    import glob
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        out = {}
+        for dom in ("sclk", "mclk", "fclk", "socclk"):
             try:
-                return _compact_clocks(json.loads(r.stdout))
-            except ValueError:
-                return r.stdout.strip()[:2000]
+                lines = open(os.path.join(dev, f"pp_dpm_{dom}")).read().splitlines()
+            except OSError:
+                continue
+            for ln in lines:
+                if ln.rstrip().endswith("*"):
+                    m = re.search(r"(\d+)\s*[Mm][Hh]z", ln)
+                    if m:
+                        out[dom] = int(m.group(1))
+        if out:
+            return out
     return None
-
-
-def _compact_clocks(j):
-    """{domain: current MHz} from amd-smi's per-GPU clock records (the
-    graphics clock of every XCD, memory, fabric, ...); other layouts as
-    they came."""
-    try:
-        clk = j["gpu_data"][0]["clock"] if isinstance(j, dict) else j[0]["clock"]
-        return {k: v["clk"]["value"] for k, v in clk.items()
-                if isinstance(v, dict) and isinstance(v.get("clk"), dict) and "value" in v["clk"]}
-    except (KeyError, IndexError, TypeError):
-        return j
 
 
 def cold_steps(step, n, torch):
@@ -601,8 +593,8 @@ def train_section(args, cfg, d, torch, R, synth):
         # written by the same launches (into the same buffers every step)
         for k in ("w13", "w2", "sw13", "sw2"):
             if k in d:
-                R.quant_weight_128x128_e4m3(d[k], q=w[k + "q"], scale=w[k + "s"], qt=wt[k + "tq"],
-                                            scale_t=wt[k + "ts"])
+                R.quant_weight_128x128_e4m3_t(d[k], q=w[k + "q"], scale=w[k + "s"], qt=wt[k + "tq"],
+                                              scale_t=wt[k + "ts"])
         m("quantize_and_transpose_weights")
         fwd(d["x"], d["logits"], bias)
         m("forward")

@@ -167,16 +167,28 @@ MOE_API moe_status quant_act_1x128_e4m3(const void* x, moe_dtype x_dtype, int64_
  *         anchored at (0, 0)
  *  q      u8  [G, rows, cols]            (out)
  *  scale  f32 [G, rows/128, cols/128]    (out)
- *  qt, scale_t  u8 [G, cols, rows], f32 [G, cols/128, rows/128] (out,
- *         optional, both or neither NULL): the same codes and scales block-
- *         transposed in the same pass, bit-identical to fp8_block_transpose of
- *         (q, scale) -- the backward's operand without a second read of q
- *                                                        [KANANA-FP8]
- * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN.
+ *  G == 0 launches nothing.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED (dtype, 2^31 or
+ *         more blocks), MOE_ERR_ALIGN.
  */
 MOE_API moe_status quant_weight_128x128_e4m3(const void* w, moe_dtype w_dtype, int32_t G, int32_t rows,
-                                     int32_t cols, uint8_t* q, float* scale, uint8_t* qt, float* scale_t,
-                                     void* stream);
+                                     int32_t cols, uint8_t* q, float* scale, void* stream);
+
+/*
+ * quant_weight_128x128_e4m3_t -- quant_weight_128x128_e4m3 that also writes
+ * the block-transposed codes and scales in the same pass: bit-identical to
+ * quant_weight_128x128_e4m3 followed by fp8_block_transpose of (q, scale),
+ * without the second read of q (the backward's operand: only the forward
+ * FP8 weights are kept and the backward transposes them).     [KANANA-FP8]
+ *
+ *  w, w_dtype, G, rows, cols, q, scale: as quant_weight_128x128_e4m3
+ *  qt       u8  [G, cols, rows]          (out, required)
+ *  scale_t  f32 [G, cols/128, rows/128]  (out, required)
+ * Errors: as quant_weight_128x128_e4m3; NULL qt or scale_t -> MOE_ERR_NULL.
+ */
+MOE_API moe_status quant_weight_128x128_e4m3_t(const void* w, moe_dtype w_dtype, int32_t G, int32_t rows,
+                                       int32_t cols, uint8_t* q, float* scale, uint8_t* qt, float* scale_t,
+                                       void* stream);
 
 /*
  * grouped_gemm_fp8_blockscaled -- per-group C = A . B_g^T with block-scaled
@@ -189,25 +201,39 @@ MOE_API moe_status quant_weight_128x128_e4m3(const void* w, moe_dtype w_dtype, i
  * output per chunk), in chunk order.
  *
  *  aq  u8 [M, K], as f32 [M, K/128]           activations, 1x128 tiles
- *  a_row  i32 [M] or NULL   optional row gather: row m of the grouped operand
- *         is row a_row[m] of aq / as, which then have a_rows rows (the
- *         permutation's src_token turns the token-order codes into the
- *         expert-grouped operand without a permuted copy).  Indices outside
- *         [0, a_rows) are clamped into it.  NULL: aq / as have M rows and
- *         a_rows is ignored.  With a_row, a_rows * K must be <= 2^32.
  *  bq  u8 [G, N, K], bs f32 [G, N/128, K/128] weights ([out, in] per group)
  *  group_offsets i32 [G+1] (device)           offsets[G] == M
  *  c   f32 or bf16 [M, N] (out); bf16 output is the RNE rounding of the
  *      float32 result.  Rows of empty groups do not exist; every row of C is
  *      written.
- *  Sizes: M >= 0, 1 <= G <= 1024, N % 128 == 0, K % 128 == 0.
+ *  Sizes: M >= 0 (M == 0 launches nothing), 1 <= G <= 1024, N % 128 == 0,
+ *  K % 128 == 0.
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED (G > 1024, K >
- *         65536, a gathered operand above 4 GiB), MOE_ERR_ALIGN.
+ *         65536, c_dtype), MOE_ERR_ALIGN.
  */
-MOE_API moe_status grouped_gemm_fp8_blockscaled(const uint8_t* aq, const float* as, const int32_t* a_row,
-                                        int64_t a_rows, const uint8_t* bq, const float* bs,
-                                        const int32_t* group_offsets, int32_t G, int64_t M, int32_t N,
-                                        int32_t K, void* c, moe_dtype c_dtype, void* stream);
+MOE_API moe_status grouped_gemm_fp8_blockscaled(const uint8_t* aq, const float* as, const uint8_t* bq,
+                                        const float* bs, const int32_t* group_offsets, int32_t G, int64_t M,
+                                        int32_t N, int32_t K, void* c, moe_dtype c_dtype, void* stream);
+
+/*
+ * grouped_gemm_fp8_blockscaled_gather -- grouped_gemm_fp8_blockscaled whose
+ * grouped operand is gathered by row: row m of A is row a_row[m] of aq / as
+ * (the permutation's src_token turns the token-order codes into the
+ * expert-grouped operand without writing a permuted copy; the tokens are
+ * dispatched to their experts with nothing dropped).          [DSV3-MOE]
+ *
+ *  aq  u8 [a_rows, K], as f32 [a_rows, K/128]  token-order activations
+ *  a_row  i32 [M] (device, required)   indices outside [0, a_rows) are
+ *         clamped into it; a_rows >= 1 and a_rows * K <= 2^32
+ *  bq, bs, group_offsets, G, M, N, K, c, c_dtype: as grouped_gemm_fp8_blockscaled
+ *  (same values, bit for bit, as the ungathered call on the gathered copy).
+ * Errors: as grouped_gemm_fp8_blockscaled; MOE_ERR_UNSUPPORTED for a
+ *         gathered operand above 4 GiB.
+ */
+MOE_API moe_status grouped_gemm_fp8_blockscaled_gather(const uint8_t* aq, const float* as, const int32_t* a_row,
+                                               int64_t a_rows, const uint8_t* bq, const float* bs,
+                                               const int32_t* group_offsets, int32_t G, int64_t M, int32_t N,
+                                               int32_t K, void* c, moe_dtype c_dtype, void* stream);
 
 /*
  * grouped_gemm_fp8_swiglu -- the gate|up grouped GEMM with SwiGLU and 1x128
@@ -219,7 +245,8 @@ MOE_API moe_status grouped_gemm_fp8_blockscaled(const uint8_t* aq, const float* 
  * binary32 sigmoid specification of moe_route, and quantises h in 1x128 tiles
  * along I.  The float32 G1 is never written.
  *
- *  aq, as, a_row, a_rows: as for grouped_gemm_fp8_blockscaled
+ *  aq, as, a_row, a_rows: as for grouped_gemm_fp8_blockscaled_gather; a_row
+ *         may be NULL (then aq / as have M rows and a_rows is ignored)
  *  bq  u8 [G, 2I, K]: rows [0, I) are the gate projection, [I, 2I) the up
  *  hq  u8 [M, I], hs f32 [M, I/128]   (out, in grouped row order)
  *  Sizes: I % 128 == 0, K % 128 == 0.

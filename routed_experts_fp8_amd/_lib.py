@@ -29,9 +29,14 @@ _SIGNATURES = {
                            _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p]),
     "quant_act_1x128_e4m3": (_i32, [_c_void_p, _i32, _i64, _i32, _c_void_p, _c_void_p, _c_void_p]),
     "quant_weight_128x128_e4m3": (_i32, [_c_void_p, _i32, _i32, _i32, _i32, _c_void_p, _c_void_p,
-                                         _c_void_p, _c_void_p, _c_void_p]),
-    "grouped_gemm_fp8_blockscaled": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p, _c_void_p,
-                                            _c_void_p, _i32, _i64, _i32, _i32, _c_void_p, _i32, _c_void_p]),
+                                         _c_void_p]),
+    "quant_weight_128x128_e4m3_t": (_i32, [_c_void_p, _i32, _i32, _i32, _i32, _c_void_p, _c_void_p,
+                                           _c_void_p, _c_void_p, _c_void_p]),
+    "grouped_gemm_fp8_blockscaled": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32,
+                                            _i64, _i32, _i32, _c_void_p, _i32, _c_void_p]),
+    "grouped_gemm_fp8_blockscaled_gather": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p,
+                                                   _c_void_p, _c_void_p, _i32, _i64, _i32, _i32, _c_void_p,
+                                                   _i32, _c_void_p]),
     "grouped_gemm_fp8_swiglu": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p, _c_void_p,
                                        _c_void_p, _i32, _i64, _i32, _i32, _c_void_p, _c_void_p, _c_void_p]),
     "swiglu": (_i32, [_c_void_p, _i64, _i32, _c_void_p, _c_void_p, _c_void_p]),
@@ -206,23 +211,32 @@ def quant_act_1x128_e4m3(x, q=None, scale=None):
     return q, scale
 
 
-def quant_weight_128x128_e4m3(w, q=None, scale=None, transposed=False, qt=None, scale_t=None):
-    """w float32/bf16 [G, rows, cols] -> (codes [G, rows, cols], scales [G, rows/128, cols/128]);
-    with transposed=True (or qt/scale_t given) also the block-transposed codes
-    [G, cols, rows] and scales [G, cols/128, rows/128] from the same pass:
+def quant_weight_128x128_e4m3(w, q=None, scale=None):
+    """w float32/bf16 [G, rows, cols] -> (codes [G, rows, cols], scales [G, rows/128, cols/128])."""
+    code = _dtype_code(w)
+    _need(w, "w", w.dtype)
+    G, rows, cols = w.shape
+    q = _out(q, "q", (G, rows, cols), torch.uint8, w.device)
+    scale = _out(scale, "scale", (G, rows // 128, cols // 128), torch.float32, w.device)
+    _check("quant_weight_128x128_e4m3", lib.quant_weight_128x128_e4m3(
+        _p(w), code, G, rows, cols, _p(q), _p(scale), _stream()))
+    return q, scale
+
+
+def quant_weight_128x128_e4m3_t(w, q=None, scale=None, qt=None, scale_t=None):
+    """As quant_weight_128x128_e4m3, plus the block-transposed codes
+    [G, cols, rows] and scales [G, cols/128, rows/128] from the same pass
     -> (q, scale, qt, scale_t)."""
     code = _dtype_code(w)
     _need(w, "w", w.dtype)
     G, rows, cols = w.shape
     q = _out(q, "q", (G, rows, cols), torch.uint8, w.device)
     scale = _out(scale, "scale", (G, rows // 128, cols // 128), torch.float32, w.device)
-    transposed = transposed or qt is not None or scale_t is not None
-    if transposed:
-        qt = _out(qt, "qt", (G, cols, rows), torch.uint8, w.device)
-        scale_t = _out(scale_t, "scale_t", (G, cols // 128, rows // 128), torch.float32, w.device)
-    _check("quant_weight_128x128_e4m3", lib.quant_weight_128x128_e4m3(
+    qt = _out(qt, "qt", (G, cols, rows), torch.uint8, w.device)
+    scale_t = _out(scale_t, "scale_t", (G, cols // 128, rows // 128), torch.float32, w.device)
+    _check("quant_weight_128x128_e4m3_t", lib.quant_weight_128x128_e4m3_t(
         _p(w), code, G, rows, cols, _p(q), _p(scale), _p(qt), _p(scale_t), _stream()))
-    return (q, scale, qt, scale_t) if transposed else (q, scale)
+    return q, scale, qt, scale_t
 
 
 def _gemm_operands(aq, as_, bq, bs, offsets, a_row):
@@ -243,15 +257,30 @@ def _gemm_operands(aq, as_, bq, bs, offsets, a_row):
     return M, K, G, N, A
 
 
-def grouped_gemm_fp8_blockscaled(aq, as_, bq, bs, offsets, out_dtype=torch.float32, c=None, a_row=None):
-    """C[M, N] = per-group A . B_g^T with block scales (float32 or bf16 output;
-    the type of ``c`` when given, else ``out_dtype``).
-    a_row (int32 [M]), if given, gathers row m of A from aq[a_row[m]]."""
-    M, K, G, N, A = _gemm_operands(aq, as_, bq, bs, offsets, a_row)
+def _c_out(c, out_dtype, M, N, device):
     if c is not None and c.dtype in (torch.float32, torch.bfloat16):
         out_dtype = c.dtype                       # a given output buffer sets the type
-    c = _out(c, "c", (M, N), out_dtype, aq.device)
+    return _out(c, "c", (M, N), out_dtype, device)
+
+
+def grouped_gemm_fp8_blockscaled(aq, as_, bq, bs, offsets, out_dtype=torch.float32, c=None):
+    """C[M, N] = per-group A . B_g^T with block scales (float32 or bf16 output;
+    the type of ``c`` when given, else ``out_dtype``)."""
+    M, K, G, N, A = _gemm_operands(aq, as_, bq, bs, offsets, None)
+    c = _c_out(c, out_dtype, M, N, aq.device)
     _check("grouped_gemm_fp8_blockscaled", lib.grouped_gemm_fp8_blockscaled(
+        _p(aq), _p(as_), _p(bq), _p(bs), _p(offsets), G, M, N, K, _p(c), _dtype_code(c), _stream()))
+    return c
+
+
+def grouped_gemm_fp8_blockscaled_gather(aq, as_, a_row, bq, bs, offsets, out_dtype=torch.float32, c=None):
+    """As grouped_gemm_fp8_blockscaled with row m of A read from aq[a_row[m]]
+    (a_row int32 [M]; aq / as in token order)."""
+    if a_row is None:
+        raise ValueError("a_row is required")
+    M, K, G, N, A = _gemm_operands(aq, as_, bq, bs, offsets, a_row)
+    c = _c_out(c, out_dtype, M, N, aq.device)
+    _check("grouped_gemm_fp8_blockscaled_gather", lib.grouped_gemm_fp8_blockscaled_gather(
         _p(aq), _p(as_), _p(a_row), A, _p(bq), _p(bs), _p(offsets), G, M, N, K, _p(c), _dtype_code(c),
         _stream()))
     return c

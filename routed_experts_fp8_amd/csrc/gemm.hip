@@ -460,13 +460,12 @@ moe_status check_gemm_args(const uint8_t* aq, const float* as, const int32_t* a_
 
 using namespace moefp8;
 
-extern "C" moe_status grouped_gemm_fp8_blockscaled(const uint8_t* aq, const float* as,
-                                                   const int32_t* a_row, int64_t a_rows,
-                                                   const uint8_t* bq, const float* bs,
-                                                   const int32_t* group_offsets, int32_t G,
-                                                   int64_t M, int32_t N, int32_t K, void* c,
-                                                   moe_dtype c_dtype, void* stream) {
-  clear_detail();
+namespace moefp8 {
+namespace {
+
+moe_status gemm_entry(const uint8_t* aq, const float* as, const int32_t* a_row, int64_t a_rows,
+                      const uint8_t* bq, const float* bs, const int32_t* group_offsets, int32_t G, int64_t M,
+                      int32_t N, int32_t K, void* c, moe_dtype c_dtype, void* stream, const char* what) {
   MOE_REQUIRE(c_dtype == MOE_F32 || c_dtype == MOE_BF16, MOE_ERR_UNSUPPORTED, "c_dtype %d", (int)c_dtype);
   moe_status stt = check_gemm_args(aq, as, a_row, a_rows, bq, bs, group_offsets, G, M, N, K);
   if (stt != MOE_OK || M == 0) return stt;
@@ -474,10 +473,32 @@ extern "C" moe_status grouped_gemm_fp8_blockscaled(const uint8_t* aq, const floa
   MOE_REQUIRE(aligned(c, 16), MOE_ERR_ALIGN, "c needs 16-byte alignment");
   hipStream_t st = as_stream(stream);
   if (c_dtype == MOE_F32)
-    return launch_gemm<OUT_F32>(aq, as, a_row, a_rows, bq, bs, group_offsets, G, M, N, K, c, nullptr, st,
-                                "grouped_gemm_fp8_blockscaled");
-  return launch_gemm<OUT_BF16>(aq, as, a_row, a_rows, bq, bs, group_offsets, G, M, N, K, c, nullptr, st,
-                               "grouped_gemm_fp8_blockscaled");
+    return launch_gemm<OUT_F32>(aq, as, a_row, a_rows, bq, bs, group_offsets, G, M, N, K, c, nullptr, st, what);
+  return launch_gemm<OUT_BF16>(aq, as, a_row, a_rows, bq, bs, group_offsets, G, M, N, K, c, nullptr, st, what);
+}
+
+}  // namespace
+}  // namespace moefp8
+
+extern "C" moe_status grouped_gemm_fp8_blockscaled(const uint8_t* aq, const float* as, const uint8_t* bq,
+                                                   const float* bs, const int32_t* group_offsets, int32_t G,
+                                                   int64_t M, int32_t N, int32_t K, void* c, moe_dtype c_dtype,
+                                                   void* stream) {
+  clear_detail();
+  return gemm_entry(aq, as, nullptr, 0, bq, bs, group_offsets, G, M, N, K, c, c_dtype, stream,
+                    "grouped_gemm_fp8_blockscaled");
+}
+
+extern "C" moe_status grouped_gemm_fp8_blockscaled_gather(const uint8_t* aq, const float* as,
+                                                          const int32_t* a_row, int64_t a_rows,
+                                                          const uint8_t* bq, const float* bs,
+                                                          const int32_t* group_offsets, int32_t G, int64_t M,
+                                                          int32_t N, int32_t K, void* c, moe_dtype c_dtype,
+                                                          void* stream) {
+  clear_detail();
+  MOE_REQUIRE(a_row != nullptr || M == 0, MOE_ERR_NULL, "a_row is required");
+  return gemm_entry(aq, as, a_row, a_rows, bq, bs, group_offsets, G, M, N, K, c, c_dtype, stream,
+                    "grouped_gemm_fp8_blockscaled_gather");
 }
 
 extern "C" moe_status grouped_gemm_fp8_swiglu(const uint8_t* aq, const float* as, const int32_t* a_row,

@@ -188,16 +188,17 @@ extern "C" moe_status quant_act_1x128_e4m3(const void* x, moe_dtype x_dtype, int
   return after_launch("quant_act_1x128_e4m3", st);
 }
 
-extern "C" moe_status quant_weight_128x128_e4m3(const void* w, moe_dtype w_dtype, int32_t G,
-                                                int32_t rows, int32_t cols, uint8_t* q,
-                                                float* scale, uint8_t* qt, float* scale_t, void* stream) {
-  clear_detail();
+namespace moefp8 {
+namespace {
+
+moe_status quant_weight_impl(const void* w, moe_dtype w_dtype, int32_t G, int32_t rows, int32_t cols,
+                             uint8_t* q, float* scale, uint8_t* qt, float* scale_t, void* stream,
+                             const char* what) {
   MOE_REQUIRE(w_dtype == MOE_F32 || w_dtype == MOE_BF16, MOE_ERR_UNSUPPORTED, "w_dtype %d", (int)w_dtype);
   MOE_REQUIRE(G >= 0 && rows > 0 && cols > 0 && rows % 128 == 0 && cols % 128 == 0, MOE_ERR_SHAPE,
               "G=%d rows=%d cols=%d (rows, cols positive multiples of 128)", G, rows, cols);
   if (G == 0) return MOE_OK;
   MOE_REQUIRE(w && q && scale, MOE_ERR_NULL, "w, q and scale are required");
-  MOE_REQUIRE((qt == nullptr) == (scale_t == nullptr), MOE_ERR_NULL, "qt and scale_t go together");
   MOE_REQUIRE(aligned(w, 16) && aligned(q, 16) && aligned(scale, 4) && aligned(qt, 16) && aligned(scale_t, 4),
               MOE_ERR_ALIGN, "w, q and qt need 16-byte alignment, the scales 4-byte");
   const int64_t nblk = (int64_t)G * (rows / 128) * (cols / 128);
@@ -211,5 +212,24 @@ extern "C" moe_status quant_weight_128x128_e4m3(const void* w, moe_dtype w_dtype
     if (qt) MOE_QW_LAUNCH(float, true); else MOE_QW_LAUNCH(float, false);
   }
 #undef MOE_QW_LAUNCH
-  return after_launch("quant_weight_128x128_e4m3", st);
+  return after_launch(what, st);
+}
+
+}  // namespace
+}  // namespace moefp8
+
+extern "C" moe_status quant_weight_128x128_e4m3(const void* w, moe_dtype w_dtype, int32_t G, int32_t rows,
+                                                int32_t cols, uint8_t* q, float* scale, void* stream) {
+  clear_detail();
+  return quant_weight_impl(w, w_dtype, G, rows, cols, q, scale, nullptr, nullptr, stream,
+                           "quant_weight_128x128_e4m3");
+}
+
+extern "C" moe_status quant_weight_128x128_e4m3_t(const void* w, moe_dtype w_dtype, int32_t G, int32_t rows,
+                                                  int32_t cols, uint8_t* q, float* scale, uint8_t* qt,
+                                                  float* scale_t, void* stream) {
+  clear_detail();
+  if (G > 0) MOE_REQUIRE(qt && scale_t, MOE_ERR_NULL, "qt and scale_t are required");
+  return quant_weight_impl(w, w_dtype, G, rows, cols, q, scale, qt, scale_t, stream,
+                           "quant_weight_128x128_e4m3_t");
 }

@@ -35,7 +35,7 @@ def quantize_weights(w13, w2, sw13=None, sw2=None, transposed=False):
     q, t = {}, {}
     mats = [("w13", w13), ("w2", w2)] + ([("sw13", sw13), ("sw2", sw2)] if sw13 is not None else [])
     for k, m in mats:
-        r = L.quant_weight_128x128_e4m3(m, transposed=transposed)
+        r = L.quant_weight_128x128_e4m3_t(m) if transposed else L.quant_weight_128x128_e4m3(m)
         q[k + "q"], q[k + "s"] = r[0], r[1]
         if transposed:
             t[k + "tq"], t[k + "ts"] = r[2], r[3]
@@ -88,7 +88,10 @@ class MoEForward:
         if self.fused:
             L.grouped_gemm_fp8_swiglu(aq, as_, w13q, w13s, offsets, hq=hq, hs=hs, a_row=a_row)
         else:
-            L.grouped_gemm_fp8_blockscaled(aq, as_, w13q, w13s, offsets, c=c1, a_row=a_row)
+            if a_row is None:
+                L.grouped_gemm_fp8_blockscaled(aq, as_, w13q, w13s, offsets, c=c1)
+            else:
+                L.grouped_gemm_fp8_blockscaled_gather(aq, as_, a_row, w13q, w13s, offsets, c=c1)
             L.swiglu(c1, hq=hq, hs=hs)
         mark("gemm1")
         L.grouped_gemm_fp8_blockscaled(hq, hs, w2q, w2s, offsets, c=c2)

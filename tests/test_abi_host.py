@@ -23,8 +23,15 @@ N0 = None
 S = None                              # null stream
 
 
+# the eight operations of the layer's problem statement (routing, permutation,
+# the two quantisers, the block-scaled grouped GEMM, SwiGLU, the combine and
+# the block transpose)
+CORE = ["moe_route", "moe_permute", "quant_act_1x128_e4m3", "quant_weight_128x128_e4m3",
+        "grouped_gemm_fp8_blockscaled", "swiglu", "moe_combine", "fp8_block_transpose"]
+
+
 def test_every_declared_symbol_is_exported():
-    assert len(DECLARED) == 20, DECLARED
+    assert set(CORE) <= set(DECLARED), DECLARED
     for name in DECLARED:
         assert hasattr(L.lib, name), name
     assert set(DECLARED) == set(L._SIGNATURES)
@@ -59,13 +66,20 @@ def test_quant_errors():
     assert f(PM, 1, 4, 128, P, P, S) == ALIGN
     assert f(N0, 0, 0, 128, N0, N0, S) == OK          # empty: nothing to do
     g = L.lib.quant_weight_128x128_e4m3
-    assert g(P, 0, 2, 100, 128, P, P, N0, N0, S) == SHAPE
-    assert g(P, 0, 2, 128, 130, P, P, N0, N0, S) == SHAPE
-    assert g(P, 0, 2, 128, 128, N0, P, N0, N0, S) == NULL
-    assert g(P, 0, 2, 128, 128, P, P, P, N0, S) == NULL                  # qt without scale_t
-    assert g(P, 0, 2, 128, 128, PM, P, N0, N0, S) == ALIGN
-    assert g(P, 0, 2, 128, 128, P, P, PM, P, S) == ALIGN                 # qt 16-byte
-    assert g(N0, 0, 0, 128, 128, N0, N0, N0, N0, S) == OK
+    assert g(P, 0, 2, 100, 128, P, P, S) == SHAPE
+    assert g(P, 0, 2, 128, 130, P, P, S) == SHAPE
+    assert g(P, 0, 2, 128, 128, N0, P, S) == NULL
+    assert g(P, 0, 2, 128, 128, PM, P, S) == ALIGN
+    assert g(P, 7, 2, 128, 128, P, P, S) == UNSUP
+    assert g(N0, 0, 0, 128, 128, N0, N0, S) == OK
+    t = L.lib.quant_weight_128x128_e4m3_t
+    assert t(P, 0, 2, 100, 128, P, P, P, P, S) == SHAPE
+    assert t(P, 0, 2, 128, 128, N0, P, P, P, S) == NULL
+    assert t(P, 0, 2, 128, 128, P, P, P, N0, S) == NULL                  # qt without scale_t
+    assert t(P, 0, 2, 128, 128, P, P, N0, P, S) == NULL                  # scale_t without qt
+    assert t(P, 0, 2, 128, 128, PM, P, P, P, S) == ALIGN
+    assert t(P, 0, 2, 128, 128, P, P, PM, P, S) == ALIGN                 # qt 16-byte
+    assert t(N0, 0, 0, 128, 128, N0, N0, N0, N0, S) == OK
 
 
 def test_route_errors():
@@ -96,20 +110,25 @@ def test_permute_errors():
 
 def test_gemm_errors():
     f = L.lib.grouped_gemm_fp8_blockscaled
-    assert f(P, P, N0, 0, P, P, P, 4, 64, 100, 128, P, 0, S) == SHAPE
-    assert f(P, P, N0, 0, P, P, P, 4, 64, 128, 130, P, 0, S) == SHAPE
-    assert f(P, P, N0, 0, P, P, P, 2048, 64, 128, 128, P, 0, S) == UNSUP            # G > 1024
-    assert f(P, P, N0, 0, P, P, P, 4, 64, 128, 65536 + 128, P, 0, S) == UNSUP       # K > 65536
-    assert f(P, P, N0, 0, P, P, P, 0, 64, 128, 128, P, 0, S) == SHAPE
-    assert f(P, P, N0, 0, P, P, N0, 4, 64, 128, 128, P, 0, S) == NULL
-    assert f(P, P, N0, 0, P, P, P, 4, 64, 128, 128, N0, 0, S) == NULL
-    assert f(PM, P, N0, 0, P, P, P, 4, 64, 128, 128, P, 0, S) == ALIGN
-    assert f(P, P, N0, 0, P, P, P, 4, 64, 128, 128, P, 5, S) == UNSUP
-    assert f(N0, N0, N0, 0, N0, N0, P, 4, 0, 128, 128, N0, 0, S) == OK           # M = 0
-    # row gather: misaligned index array, no source rows, source above 4 GiB
+    assert f(P, P, P, P, P, 4, 64, 100, 128, P, 0, S) == SHAPE
+    assert f(P, P, P, P, P, 4, 64, 128, 130, P, 0, S) == SHAPE
+    assert f(P, P, P, P, P, 2048, 64, 128, 128, P, 0, S) == UNSUP            # G > 1024
+    assert f(P, P, P, P, P, 4, 64, 128, 65536 + 128, P, 0, S) == UNSUP       # K > 65536
+    assert f(P, P, P, P, P, 0, 64, 128, 128, P, 0, S) == SHAPE
+    assert f(P, P, P, P, N0, 4, 64, 128, 128, P, 0, S) == NULL
+    assert f(P, P, P, P, P, 4, 64, 128, 128, N0, 0, S) == NULL
+    assert f(PM, P, P, P, P, 4, 64, 128, 128, P, 0, S) == ALIGN
+    assert f(P, P, P, P, P, 4, 64, 128, 128, P, 5, S) == UNSUP
+    assert f(N0, N0, N0, N0, P, 4, 0, 128, 128, N0, 0, S) == OK           # M = 0
+    # row gather: no index array, misaligned index array, no source rows,
+    # source above 4 GiB
+    f = L.lib.grouped_gemm_fp8_blockscaled_gather
+    assert f(P, P, N0, 16, P, P, P, 4, 64, 128, 128, P, 0, S) == NULL
     assert f(P, P, ctypes.c_void_p(0x10002), 16, P, P, P, 4, 64, 128, 128, P, 0, S) == ALIGN
     assert f(P, P, P, 0, P, P, P, 4, 64, 128, 128, P, 0, S) == SHAPE
     assert f(P, P, P, 1 << 26, P, P, P, 4, 64, 128, 128, P, 0, S) == UNSUP
+    assert f(P, P, P, 16, P, P, P, 4, 64, 100, 128, P, 0, S) == SHAPE
+    assert f(N0, N0, N0, 0, N0, N0, P, 4, 0, 128, 128, N0, 0, S) == OK    # M = 0
     g = L.lib.grouped_gemm_fp8_swiglu
     assert g(P, P, N0, 0, P, P, P, 4, 64, 100, 128, P, P, S) == SHAPE
     assert g(P, P, N0, 0, P, P, P, 4, 64, 128, 128, P, N0, S) == NULL
@@ -238,3 +257,25 @@ def test_product_path_does_not_use_the_oracle():
                 assert not any(a.name.split(".")[0] == "oracle" for a in node.names), f
             if isinstance(node, ast.ImportFrom):
                 assert (node.module or "").split(".")[0] != "oracle", f
+
+
+def test_c_caller_of_the_eight_operations(tmp_path):
+    """A C program that declares the eight operations' prototypes itself (not
+    from include/moefp8.h) links against libmoefp8.so and gets the documented
+    status from one failing (or empty) call of each: a prototype that drifted
+    would shift its arguments and miss the expected codes."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    src = os.path.join(ROOT, "tests", "abi_c", "caller_8ops.c")
+    libdir = os.path.dirname(L.LIB_PATH)
+    exe = str(tmp_path / "caller_8ops")
+    r = subprocess.run([cc, "-std=c99", "-Wall", "-Werror", "-o", exe, src, "-L", libdir, "-lmoefp8",
+                        f"-Wl,-rpath,{libdir}"], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    print(r.stdout)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "PASSED" in r.stdout

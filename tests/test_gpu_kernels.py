@@ -132,7 +132,7 @@ def test_quant_weight_with_transposed_copy(G, rows, cols, dtype):
     w = (RNG.standard_normal((G, rows, cols)) * 0.02).astype(np.float32)
     w[0, :128, :128] = 0.0
     wt = to_dev(w).to(dtype)
-    q, s, qt, st = R.quant_weight_128x128_e4m3(wt, transposed=True)
+    q, s, qt, st = R.quant_weight_128x128_e4m3_t(wt)
     qo, so = O.quant_weight_128x128(np_(wt))
     assert np.array_equal(np_(q), qo) and np.array_equal(np_(s), so)
     qto, sto = O.block_transpose(qo, so)
@@ -313,7 +313,7 @@ def test_grouped_gemm_many_tiles_short_k(K):
     src_q, src_s = np.empty_like(aq), np.empty_like(as_)
     src_q[perm], src_s[perm] = aq, as_
     a_row = to_dev(perm.astype(np.int32))
-    cg = R.grouped_gemm_fp8_blockscaled(to_dev(src_q), to_dev(src_s), args[2], args[3], args[4], a_row=a_row)
+    cg = R.grouped_gemm_fp8_blockscaled_gather(to_dev(src_q), to_dev(src_s), a_row, args[2], args[3], args[4])
     assert torch.equal(cg, c)
     hg, hsg = R.grouped_gemm_fp8_swiglu(to_dev(src_q), to_dev(src_s), args[2], args[3], args[4], a_row=a_row)
     assert torch.equal(hg, hq) and torch.equal(hsg, hs)
@@ -333,7 +333,7 @@ def test_grouped_gemm_row_gather(K):
     off = rand_offsets(RNG, sizes)
     aq, as_ = src_q[a_row_np], src_s[a_row_np]
     w = [to_dev(v) for v in (bq, bs, off)]
-    c = R.grouped_gemm_fp8_blockscaled(to_dev(src_q), to_dev(src_s), *w, a_row=to_dev(a_row_np))
+    c = R.grouped_gemm_fp8_blockscaled_gather(to_dev(src_q), to_dev(src_s), to_dev(a_row_np), *w)
     assert torch.equal(c, R.grouped_gemm_fp8_blockscaled(to_dev(aq), to_dev(as_), *w))
     C, Mag = O.grouped_gemm(aq, as_, bq, bs, off)
     assert_gemm_close(np_(c), C, Mag)
