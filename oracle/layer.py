@@ -32,33 +32,28 @@ def route(logits, bias, rc):
     return route_softmax_grouped(logits, rc["n_groups"], rc["k_per_group"])
 
 
-def _expert_ffn(aq, as_, offsets, w13q, w13s, w2q, w2s, h_forced=None):
+def _expert_ffn(aq, as_, offsets, w13q, w13s, w2q, w2s):
     c1, mag1 = grouped_gemm(aq, as_, w13q, w13s, offsets, with_mag=True)
-    if h_forced is None:
-        hq, hs, _ = swiglu_quant(c1.astype(np.float32))
-    else:
-        hq, hs = h_forced
+    hq, hs, _ = swiglu_quant(c1.astype(np.float32))
     c2, mag2 = grouped_gemm(hq, hs, w2q, w2s, offsets, with_mag=True)
     return dict(c1=c1, mag1=mag1, hq=hq, hs=hs, c2=c2, mag2=mag2)
 
 
-def layer_forward(x, logits, bias, rc, w13q, w13s, w2q, w2s, shared=None,
-                  h_forced=None, h_forced_shared=None):
+def layer_forward(x, logits, bias, rc, w13q, w13s, w2q, w2s, shared=None):
     """x f32 [T, H]; weights already block-quantised ([G, rows, cols] codes
     and scales).  shared: None or (w13q, w13s, w2q, w2s) with G = 1.
-    h_forced / h_forced_shared: optional (hq, hs) to use in place of the
-    oracle's own quantised hidden state (teacher forcing).
+    Every intermediate is the oracle's own (nothing is taken from outside).
     Returns a dict of every intermediate and y (float64 bf16 values, bits)."""
     E = w13q.shape[0]
     idx, gate = route(logits, bias, rc)
     xq, xs = quant_act_1x128(x)
     perm = permute(idx, E, xq, xs)
-    routed = _expert_ffn(perm["aq"], perm["as"], perm["offsets"], w13q, w13s, w2q, w2s, h_forced)
+    routed = _expert_ffn(perm["aq"], perm["as"], perm["offsets"], w13q, w13s, w2q, w2s)
     out = dict(topk_idx=idx, topk_gate=gate, xq=xq, xs=xs, **perm, **routed)
     S = None
     if shared is not None:
         T = x.shape[0]
-        sh = _expert_ffn(xq, xs, np.array([0, T], np.int32), *shared, h_forced=h_forced_shared)
+        sh = _expert_ffn(xq, xs, np.array([0, T], np.int32), *shared)
         S = sh["c2"]
         out.update({"shared_" + k: v for k, v in sh.items()})
     y, y_bits = combine_ref(routed["c2"], perm["dst_row"], gate, S)
