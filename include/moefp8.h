@@ -113,6 +113,19 @@ MOE_API moe_status moe_route(const float* logits, const float* bias, int32_t T, 
                      int32_t normalize_topk, int32_t* topk_idx, float* topk_gate, void* stream);
 
 /*
+ * moe_sigmoid_f32 -- y = sigmoid(x) elementwise with the binary32 sigmoid
+ * specification moe_route applies to the affinity scores (and SwiGLU to its
+ * gate), so that specification can be checked input by input.   [DSV3-MOE]
+ *
+ *  x, y   f32 [n] (device; y may equal x), n >= 0 (n == 0 launches nothing).
+ *  Every finite or infinite input is defined; NaN inputs give unspecified
+ *  values.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (n < 0), MOE_ERR_ALIGN (x, y 16-byte),
+ *         MOE_ERR_UNSUPPORTED (n >= 2^41).
+ */
+MOE_API moe_status moe_sigmoid_f32(const float* x, int64_t n, float* y, void* stream);
+
+/*
  * moe_permute_workspace_size -- bytes of device workspace moe_permute needs
  * for (T, K, E).  Host-only; never touches the device.
  */

@@ -40,6 +40,11 @@ Sources, cited in every function by these keys:
               global softmax and unselected experts score 0, which makes the
               Imbalance Score 0 by construction.
 
+``oracle.native`` holds plain C forms of the weight quantiser, the E4M3
+encoder, the GEMM rows and the sigmoid (``oracle_c.c``), for full-size
+checks; they restate the numpy definitions step for step and are held to
+them bit for bit by ``tests/test_oracle_native.py``.
+
 Readings of points the pages leave open (format, rounding, tie-break, gate
 normalisation, SwiGLU) are stated at the function that takes them.
 

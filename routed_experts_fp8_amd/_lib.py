@@ -24,6 +24,7 @@ _SIGNATURES = {
     "moe_last_error_detail": (ctypes.c_char_p, []),
     "moe_route": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
                          _c_void_p, _c_void_p, _c_void_p]),
+    "moe_sigmoid_f32": (_i32, [_c_void_p, _i64, _c_void_p, _c_void_p]),
     "moe_permute_workspace_size": (_i32, [_i32, _i32, _i32, ctypes.POINTER(_sz)]),
     "moe_permute": (_i32, [_c_void_p, _i32, _i32, _i32, _c_void_p, _c_void_p, _i32, _c_void_p,
                            _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p]),
@@ -161,14 +162,22 @@ def moe_route(logits, bias, K, mode="sigmoid_bias", n_groups=1, k_per_group=None
     return idx, gate
 
 
+def moe_sigmoid_f32(x, y=None):
+    """y = sigmoid(x) elementwise (float32, any shape), the routing's binary32
+    sigmoid."""
+    _need(x, "x", torch.float32)
+    y = _out(y, "y", tuple(x.shape), torch.float32, x.device)
+    _check("moe_sigmoid_f32", lib.moe_sigmoid_f32(_p(x), x.numel(), _p(y), _stream()))
+    return y
+
+
 def moe_permute_workspace_size(T, K, E):
     n = _sz(0)
     _check("moe_permute_workspace_size", lib.moe_permute_workspace_size(T, K, E, ctypes.byref(n)))
     return n.value
 
 
-def moe_permute(topk_idx, E, xq=None, xs=None, out=None, workspace=None):
-    """-> dict(offsets [E+1], dst_row [T, K], src_token [T*K], aq, as)."""
+def _permute_outputs(topk_idx, E, xq, xs, out):
     _need(topk_idx, "topk_idx", torch.int32)
     T, K = topk_idx.shape
     dev = topk_idx.device
@@ -188,9 +197,15 @@ def moe_permute(topk_idx, E, xq=None, xs=None, out=None, workspace=None):
     if xq is not None:
         res["aq"] = _out(out.get("aq"), "aq", (T * K, H), torch.uint8, dev)
         res["as"] = _out(out.get("as"), "as", (T * K, H // 128), torch.float32, dev)
+    return T, K, H, res
+
+
+def moe_permute(topk_idx, E, xq=None, xs=None, out=None, workspace=None):
+    """-> dict(offsets [E+1], dst_row [T, K], src_token [T*K], aq, as)."""
+    T, K, H, res = _permute_outputs(topk_idx, E, xq, xs, out)
     need = moe_permute_workspace_size(T, K, E)
     if workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = torch.empty(need, dtype=torch.uint8, device=topk_idx.device)
     _need(workspace, "workspace", torch.uint8)
     _check("moe_permute", lib.moe_permute(
         _p(topk_idx), T, K, E, _p(xq), _p(xs), H, _p(res["offsets"]), _p(res["dst_row"]),

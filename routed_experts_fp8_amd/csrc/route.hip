@@ -46,6 +46,20 @@ __device__ __forceinline__ Cand wave_argmax(Cand c) {
   return c;
 }
 
+// sigmoid of every element, the routing's own device function (the same
+// binary32 specification), four values per lane.
+__global__ __launch_bounds__(256) void sigmoid_kernel(const float* __restrict__ x, int64_t n,
+                                                      float* __restrict__ y) {
+  const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i + 4 <= n) {
+    const float4 v = *reinterpret_cast<const float4*>(x + i);
+    *reinterpret_cast<float4*>(y + i) =
+        make_float4(spec_sigmoid(v.x), spec_sigmoid(v.y), spec_sigmoid(v.z), spec_sigmoid(v.w));
+  } else {
+    for (int64_t j = i; j < n; ++j) y[j] = spec_sigmoid(x[j]);
+  }
+}
+
 template <int PL>
 __global__ __launch_bounds__(256) void route_sigmoid_kernel(const float* __restrict__ logits,
                                                             const float* __restrict__ bias, int T,
@@ -229,4 +243,17 @@ extern "C" moe_status moe_route(const float* logits, const float* bias, int32_t 
     launch_route<kMaxPerLane>(logits, bias, T, E, K, G, Kp, mode, normalize_topk, topk_idx,
                               topk_gate, st);
   return after_launch("moe_route", st);
+}
+
+extern "C" moe_status moe_sigmoid_f32(const float* x, int64_t n, float* y, void* stream) {
+  clear_detail();
+  MOE_REQUIRE(n >= 0, MOE_ERR_SHAPE, "n=%lld", (long long)n);
+  if (n == 0) return MOE_OK;
+  MOE_REQUIRE(x && y, MOE_ERR_NULL, "x and y are required");
+  MOE_REQUIRE(aligned(x, 16) && aligned(y, 16), MOE_ERR_ALIGN, "x and y need 16-byte alignment");
+  const int64_t blocks = (n + 1023) / 1024;
+  MOE_REQUIRE(blocks < (1LL << 31), MOE_ERR_UNSUPPORTED, "n=%lld too large", (long long)n);
+  hipStream_t st = as_stream(stream);
+  sigmoid_kernel<<<(unsigned)blocks, 256, 0, st>>>(x, n, y);
+  return after_launch("moe_sigmoid_f32", st);
 }

@@ -279,3 +279,13 @@ def test_c_caller_of_the_eight_operations(tmp_path):
     print(r.stdout)
     assert r.returncode == 0, r.stdout + r.stderr
     assert "PASSED" in r.stdout
+
+
+def test_sigmoid_errors():
+    f = L.lib.moe_sigmoid_f32
+    assert f(P, -1, P, S) == SHAPE
+    assert f(N0, 16, P, S) == NULL
+    assert f(PM, 16, P, S) == ALIGN
+    assert f(P, 1 << 41, P, S) == UNSUP
+    assert f(N0, 0, N0, S) == OK
+
