@@ -160,6 +160,30 @@ MOE_API moe_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t K, in
                        void* stream);
 
 /*
+ * moe_permute_noalloc -- moe_permute without a caller workspace, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation).  Same arguments, same
+ * results, bit for bit, minus (workspace, workspace_bytes).
+ *
+ * The counting scratch lives in a static device array of the library
+ * (4 MiB per GPU, held until the process ends); its address is looked up
+ * once per device on the first call there.  Every call on a GPU shares that
+ * GPU's array: calls that overlap on one GPU (different streams, or host
+ * threads) race and must be serialised by the caller.  The kernels write
+ * every scratch element before reading it, so a call needs no clearing and
+ * nothing is allocated, freed or copied.
+ *
+ * Errors: as moe_permute; MOE_ERR_WORKSPACE when (T, K, E) needs more scratch
+ *         than the array holds (moe_permute_workspace_size(T, K, E) above
+ *         4 MiB, e.g. T > 524032 at E = 256); MOE_ERR_HIP if the scratch
+ *         address cannot be obtained.
+ */
+MOE_API moe_status moe_permute_noalloc(const int32_t* topk_idx, int32_t T, int32_t K, int32_t E,
+                               const uint8_t* xq, const float* xs, int32_t H,
+                               int32_t* expert_offsets, int32_t* dst_row, int32_t* src_token,
+                               uint8_t* aq, float* as, void* stream);
+
+/*
  * quant_act_1x128_e4m3 -- per-(row, 128-column tile) FP8 quantisation of
  * activations.                                        [KANANA-FP8], [DSV3-FP8]
  *

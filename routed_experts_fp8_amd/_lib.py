@@ -28,6 +28,8 @@ _SIGNATURES = {
     "moe_permute_workspace_size": (_i32, [_i32, _i32, _i32, ctypes.POINTER(_sz)]),
     "moe_permute": (_i32, [_c_void_p, _i32, _i32, _i32, _c_void_p, _c_void_p, _i32, _c_void_p,
                            _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p]),
+    "moe_permute_noalloc": (_i32, [_c_void_p, _i32, _i32, _i32, _c_void_p, _c_void_p, _i32, _c_void_p,
+                                   _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "quant_act_1x128_e4m3": (_i32, [_c_void_p, _i32, _i64, _i32, _c_void_p, _c_void_p, _c_void_p]),
     "quant_weight_128x128_e4m3": (_i32, [_c_void_p, _i32, _i32, _i32, _i32, _c_void_p, _c_void_p,
                                          _c_void_p]),
@@ -211,6 +213,17 @@ def moe_permute(topk_idx, E, xq=None, xs=None, out=None, workspace=None):
         _p(topk_idx), T, K, E, _p(xq), _p(xs), H, _p(res["offsets"]), _p(res["dst_row"]),
         _p(res["src_token"]), _p(res.get("aq")), _p(res.get("as")), _p(workspace),
         workspace.numel(), _stream()))
+    return res
+
+
+def moe_permute_noalloc(topk_idx, E, xq=None, xs=None, out=None):
+    """moe_permute with the library's static scratch instead of a workspace
+    (the library allocates nothing; pass every output in ``out`` to allocate
+    nothing here either)."""
+    T, K, H, res = _permute_outputs(topk_idx, E, xq, xs, out)
+    _check("moe_permute_noalloc", lib.moe_permute_noalloc(
+        _p(topk_idx), T, K, E, _p(xq), _p(xs), H, _p(res["offsets"]), _p(res["dst_row"]),
+        _p(res["src_token"]), _p(res.get("aq")), _p(res.get("as")), _stream()))
     return res
 
 

@@ -16,6 +16,8 @@
 #include "device_common.h"
 #include "host_common.h"
 
+#include <mutex>
+
 namespace moefp8 {
 namespace {
 
@@ -128,17 +130,18 @@ extern "C" moe_status moe_permute_workspace_size(int32_t T, int32_t K, int32_t E
   return MOE_OK;
 }
 
-extern "C" moe_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t K, int32_t E,
-                                  const uint8_t* xq, const float* xs, int32_t H,
-                                  int32_t* expert_offsets, int32_t* dst_row, int32_t* src_token,
-                                  uint8_t* aq, float* as, void* workspace, size_t workspace_bytes,
-                                  void* stream) {
-  clear_detail();
+namespace moefp8 {
+namespace {
+
+// Argument checks shared by both entry points (host only).
+moe_status check_permute(const int32_t* topk_idx, int32_t T, int32_t K, int32_t E, const uint8_t* xq,
+                         const float* xs, int32_t H, int32_t* expert_offsets, int32_t* dst_row,
+                         int32_t* src_token, uint8_t* aq, float* as, bool* gather) {
   MOE_REQUIRE(T >= 0 && K >= 1 && E >= 1 && K <= E, MOE_ERR_SHAPE, "T=%d K=%d E=%d (need 1<=K<=E)", T, K, E);
   MOE_REQUIRE(E <= 1024, MOE_ERR_UNSUPPORTED, "E=%d > 1024", E);
   MOE_REQUIRE((int64_t)T * K < (1LL << 31), MOE_ERR_UNSUPPORTED, "T*K too large");
-  const bool gather = xq != nullptr || xs != nullptr || aq != nullptr || as != nullptr;
-  if (gather) {
+  *gather = xq != nullptr || xs != nullptr || aq != nullptr || as != nullptr;
+  if (*gather) {
     MOE_REQUIRE(xq && xs && aq && as, MOE_ERR_NULL, "xq, xs, aq and as must be all set or all NULL");
     MOE_REQUIRE(H > 0 && H % 128 == 0, MOE_ERR_SHAPE, "H=%d must be a positive multiple of 128", H);
     MOE_REQUIRE(aligned(xq, 16) && aligned(aq, 16) && aligned(xs, 4) && aligned(as, 4), MOE_ERR_ALIGN,
@@ -147,14 +150,18 @@ extern "C" moe_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t K,
   MOE_REQUIRE(expert_offsets, MOE_ERR_NULL, "expert_offsets is required");
   MOE_REQUIRE(T == 0 || (topk_idx && dst_row && src_token), MOE_ERR_NULL,
               "topk_idx, dst_row and src_token are required");
-  size_t need = 0;
-  moe_permute_workspace_size(T, K, E, &need);
-  MOE_REQUIRE(workspace_bytes >= need, MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
-  MOE_REQUIRE(workspace, MOE_ERR_NULL, "workspace is required");
-  MOE_REQUIRE(aligned(workspace, 16) && aligned(topk_idx, 4) && aligned(expert_offsets, 4) &&
-                  aligned(dst_row, 4) && aligned(src_token, 4),
-              MOE_ERR_ALIGN, "workspace needs 16-byte alignment, index arrays 4-byte");
-  hipStream_t st = as_stream(stream);
+  MOE_REQUIRE(aligned(topk_idx, 4) && aligned(expert_offsets, 4) && aligned(dst_row, 4) && aligned(src_token, 4),
+              MOE_ERR_ALIGN, "index arrays need 4-byte alignment");
+  return MOE_OK;
+}
+
+// The four launches; `workspace` holds counts [nblk, E] then base [nblk, E]
+// (every element written by the count and scan kernels before it is read,
+// so nothing needs clearing).
+moe_status launch_permute(const int32_t* topk_idx, int32_t T, int32_t K, int32_t E, const uint8_t* xq,
+                          const float* xs, int32_t H, int32_t* expert_offsets, int32_t* dst_row,
+                          int32_t* src_token, uint8_t* aq, float* as, bool gather, void* workspace,
+                          hipStream_t st, const char* what) {
   const int nblk = (T + kBT - 1) / kBT;
   int* counts = reinterpret_cast<int*>(workspace);
   int* base = counts + (size_t)nblk * E;
@@ -167,5 +174,76 @@ extern "C" moe_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t K,
   const int64_t rows = (int64_t)T * K;
   if (gather && rows > 0)
     permute_gather_kernel<<<ceil_div_u(rows, 4), 256, 0, st>>>(src_token, rows, H, xq, xs, aq, as);
-  return after_launch("moe_permute", st);
+  return after_launch(what, st);
+}
+
+// Scratch of moe_permute_noalloc: a file-scope device array (one copy per
+// GPU, held until the process ends).  Host code never uses the array's name
+// as an address: its device address is looked up once per device with
+// hipGetSymbolAddress (with that device current) and kept here.
+constexpr size_t kPermuteScratchBytes = size_t(4) << 20;
+__device__ __align__(256) uint8_t scratch[kPermuteScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+moe_status permute_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(MOE_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+  MOE_REQUIRE(dev >= 0 && dev < kMaxDevices, MOE_ERR_UNSUPPORTED, "device %d", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(MOE_ERR_HIP, "hipGetSymbolAddress(scratch): %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moefp8
+
+extern "C" moe_status moe_permute(const int32_t* topk_idx, int32_t T, int32_t K, int32_t E,
+                                  const uint8_t* xq, const float* xs, int32_t H,
+                                  int32_t* expert_offsets, int32_t* dst_row, int32_t* src_token,
+                                  uint8_t* aq, float* as, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  clear_detail();
+  bool gather = false;
+  moe_status stt = check_permute(topk_idx, T, K, E, xq, xs, H, expert_offsets, dst_row, src_token, aq, as,
+                                 &gather);
+  if (stt != MOE_OK) return stt;
+  size_t need = 0;
+  moe_permute_workspace_size(T, K, E, &need);
+  MOE_REQUIRE(workspace_bytes >= need, MOE_ERR_WORKSPACE, "workspace %zu < %zu bytes", workspace_bytes, need);
+  MOE_REQUIRE(workspace, MOE_ERR_NULL, "workspace is required");
+  MOE_REQUIRE(aligned(workspace, 16), MOE_ERR_ALIGN, "workspace needs 16-byte alignment");
+  return launch_permute(topk_idx, T, K, E, xq, xs, H, expert_offsets, dst_row, src_token, aq, as, gather,
+                        workspace, as_stream(stream), "moe_permute");
+}
+
+extern "C" moe_status moe_permute_noalloc(const int32_t* topk_idx, int32_t T, int32_t K, int32_t E,
+                                          const uint8_t* xq, const float* xs, int32_t H,
+                                          int32_t* expert_offsets, int32_t* dst_row, int32_t* src_token,
+                                          uint8_t* aq, float* as, void* stream) {
+  clear_detail();
+  bool gather = false;
+  moe_status stt = check_permute(topk_idx, T, K, E, xq, xs, H, expert_offsets, dst_row, src_token, aq, as,
+                                 &gather);
+  if (stt != MOE_OK) return stt;
+  size_t need = 0;
+  moe_permute_workspace_size(T, K, E, &need);
+  MOE_REQUIRE(need <= kPermuteScratchBytes, MOE_ERR_WORKSPACE,
+              "T=%d E=%d needs %zu bytes of scratch; the static scratch holds %zu (use moe_permute)", T, E,
+              need, kPermuteScratchBytes);
+  void* ws = nullptr;
+  stt = permute_scratch(&ws);
+  if (stt != MOE_OK) return stt;
+  return launch_permute(topk_idx, T, K, E, xq, xs, H, expert_offsets, dst_row, src_token, aq, as, gather, ws,
+                        as_stream(stream), "moe_permute_noalloc");
 }

@@ -289,3 +289,16 @@ def test_sigmoid_errors():
     assert f(P, 1 << 41, P, S) == UNSUP
     assert f(N0, 0, N0, S) == OK
 
+
+def test_permute_noalloc_errors():
+    """The scratch-array variant checks everything on the host before it
+    looks up its scratch: bad sizes, NULLs, alignment and a problem larger
+    than the static scratch never touch the device."""
+    f = L.lib.moe_permute_noalloc
+    assert f(P, 8, 9, 8, N0, N0, 0, P, P, P, N0, N0, S) == SHAPE                # K > E
+    assert f(P, 8, 2, 4096, N0, N0, 0, P, P, P, N0, N0, S) == UNSUP             # E > 1024
+    assert f(P, 8, 2, 8, P, N0, 128, P, P, P, P, P, S) == NULL                  # partial gather set
+    assert f(P, 8, 2, 8, PM, P, 128, P, P, P, P, P, S) == ALIGN
+    assert f(P, 8, 2, 8, N0, N0, 0, N0, P, P, N0, N0, S) == NULL                # no offsets
+    assert f(P, 600000, 2, 256, N0, N0, 0, P, P, P, N0, N0, S) == WS            # beyond the 4 MiB scratch
+    assert "scratch" in _detail()
