@@ -35,9 +35,18 @@
 //    of aq / as (the permutation's token index), so the permuted copy of
 //    the activations never has to be written; the indices only change the
 //    per-lane load offsets of the activation slices and scales.
+//  * Inner loop: per K chunk a wave's 4 x kTM instruction tiles run as one
+//    straight-line software pipeline over its token tiles: token tile j's
+//    four matrix products issue while the promotion FMAs of tile j - 1 run
+//    on the vector ALU and tile j + 1's operand is read from LDS (the order
+//    is pinned with scheduling-group barriers; left alone the compiler
+//    issues all products first and all FMAs after, leaving the matrix core
+//    idle during the FMAs, or hoists every read and runs out of registers).
 //  * Ragged groups: token rows past the group's end are clamped on load and
-//    never stored; 16-row instruction tiles past the end are skipped, so a
-//    group of M_g rows costs ceil(M_g / 16) tiles of matrix work.
+//    never stored; a wave with no row of the group skips the chunk, the
+//    others multiply all their instruction tiles (the clamped ones hold
+//    copies of the last row and are discarded), so one body serves every
+//    tile.
 //  * Tile table on the device, no host sync: every workgroup reads the group
 //    offsets, prefix-sums the m-tile counts in LDS (scratch aliased onto the
 //    ring) and locates its own tile; the grid is sized from the host-known
@@ -56,6 +65,7 @@
 #include "host_common.h"
 #include "lds_dma.h"
 
+#include <atomic>
 #include <type_traits>
 
 namespace moefp8 {
@@ -63,30 +73,117 @@ namespace {
 
 enum { OUT_F32 = 0, OUT_BF16 = 1, OUT_SWIGLU = 2 };
 
-constexpr int kThreads = 512;          // 8 wavefronts
-constexpr int kBN = 256;               // weight rows per workgroup tile
-constexpr int kBM = 160;               // tokens per workgroup tile
-constexpr int kWM = kBM / 2;           // tokens per wavefront
-constexpr int kTM = kWM / 16;          // 16-token instruction tiles per wavefront
-constexpr int kStages = 3;
+constexpr int kBN = 256;               // weight rows per workgroup tile (4 row-waves of 64)
 constexpr int kMaxGroups = 1024;
 constexpr int kMaxKB = 512;            // K <= 65536
-constexpr int kOffA = 0;                         // [160 rows][128 B]
-constexpr int kOffB = kBM * 128;                 // [256 rows][128 B]
-constexpr int kOffS = kOffB + kBN * 128;         // [256] float: 192 activation scales, 2 weight scales
-constexpr int kSB = 192;                         // float index of the weight-block scales in S
-constexpr int kStageBytes = kOffS + 4 * 64 * 4;  // 54272; 3 stages = 162816 B of LDS
-constexpr int kDmaPerChunk = 7;                  // per wave, see the memory pipeline notes
-constexpr int kMaxTilesPerWG = 64;              // tile-list entries per workgroup
-constexpr int kMaxNTiles = 2048;                 // n_tile field width of a tile-list entry
-constexpr int kPersistentMaxKB = 32;             // persistent launch for K <= 4096
+constexpr int kMaxTilesPerWG = 64;     // tile-list entries per workgroup
+constexpr int kMaxNTiles = 2048;       // n_tile field width of a tile-list entry
+constexpr int kPersistentMaxKB = 32;   // persistent launch for K <= 4096
 
-template <int MODE>
-__global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
+// Workgroup tile configuration: 256 weight rows x kBM tokens, 4 row-waves x
+// kWMW token-waves, each wave 64 rows x kWM tokens (4 x kTM instruction
+// tiles, 4 * kTM float32 accumulators per lane), a kStages-stage LDS ring.
+// Every wave issues exactly kDma direct global->LDS loads per K step: kWOps
+// weight slices, and kAHi activation slices (waves [0, kNHi)) or kAHi - 1
+// activation slices plus one scale load (the other waves; scale load o
+// carries the activation scales of tokens [64 o, 64 o + 64), the last one
+// the two weight-block scales; waves beyond the needed count repeat a scale
+// load, writing the same values to the same LDS words).
+template <int kWMW_, int kTM_, int kStages_, int kAHi_, int kNHi_, int kMinBlocks_>
+struct TileCfg {
+  static constexpr int kWMW = kWMW_;
+  static constexpr int kWaves = 4 * kWMW;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kMinBlocks = kMinBlocks_;
+  static constexpr int kTM = kTM_;
+  static constexpr int kWM = 16 * kTM;
+  static constexpr int kBM = kWMW * kWM;
+  static constexpr int kStages = kStages_;
+  static constexpr int kWOps = 32 / kWaves;
+  static constexpr int kAHi = kAHi_;
+  static constexpr int kNHi = kNHi_;
+  static constexpr int kNScaleOps = (kBM + 63) / 64 + 1;
+  static constexpr int kOffA = 0;                          // [kBM rows][128 B]
+  static constexpr int kOffB = kBM * 128;                  // [256 rows][128 B]
+  static constexpr int kOffS = kOffB + kBN * 128;          // activation scales, then weight-block scales
+  static constexpr int kSB = 64 * (kNScaleOps - 1);        // float index of the weight-block scales
+  static constexpr int kStageBytes = kOffS + kNScaleOps * 64 * 4;
+  static constexpr int kDma = kWOps + kAHi;
+  static constexpr int kGPT = kMaxGroups / kThreads;       // group-table entries per thread
+  static_assert(kNHi * kAHi + (kWaves - kNHi) * (kAHi - 1) == kBM / 8, "activation slices");
+  static_assert(kWaves - kNHi >= kNScaleOps, "scale loads");
+  static_assert(kStages >= 2 && (kStages - 2) * kDma < 16, "wait count");
+  static_assert(kStages * kStageBytes + kMaxTilesPerWG * 8 <= 160 * 1024, "LDS");
+};
+// 256 x 160, 8 waves, 3-stage ring (162816 B): a group a little above the
+// mean top-K load still fits one m-tile, so its weight slab streams once.
+using CfgS = TileCfg<2, 5, 3, 3, 4, 2>;
+
+// One K chunk of a wave's tile for its first NA (active) 16-token
+// instruction tiles, software-pipelined: the four chunk products of token
+// tile j go to the matrix core while the promotion FMAs of tile j - 1 run on
+// the vector ALU, and tile j + 1's operand is read from LDS meanwhile.  Each
+// accumulator still receives one fma(P_kb, sa * sb, acc) per chunk, in chunk
+// order.  tok: LDS rows of the wave's first token; sa_tok: their scales.
+template <int NA, bool kFused, int kTM>
+__device__ __forceinline__ void mma_chunk(v4f (&acc)[4][kTM], const v8i (&a_op)[4], const uint8_t* tok,
+                                          const float* sa_tok, float sb0, float sb1, uint32_t lane_lo,
+                                          uint32_t lane_hi, int l16) {
+  v8i b_cur = lds_operand(tok, lane_lo, lane_hi);
+  float sa_cur = sa_tok[l16];
+  v4f p_prev[4];
+  float sc0_prev = 0.f, sc1_prev = 0.f;
+#pragma unroll
+  for (int j = 0; j < NA; ++j) {
+    v8i b_next = b_cur;
+    float sa_next = sa_cur;
+    if (j + 1 < NA) {
+      b_next = lds_operand(tok + 16 * (j + 1) * 128, lane_lo, lane_hi);
+      sa_next = sa_tok[16 * (j + 1) + l16];
+    }
+    v4f p_cur[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p_cur[i] = mfma_chunk(a_op[i], b_cur);
+    if (j > 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float sc = (kFused && i >= 2) ? sc1_prev : sc0_prev;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[i][j - 1][v] = __builtin_fmaf(p_prev[i][v], sc, acc[i][j - 1][v]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p_prev[i] = p_cur[i];
+    sc0_prev = sa_cur * sb0;
+    sc1_prev = kFused ? sa_cur * sb1 : sc0_prev;
+    b_cur = b_next;
+    sa_cur = sa_next;
+    // order inside the stage: the next operand's LDS reads, then this tile's
+    // four matrix products, then the previous tile's promotion FMAs (which
+    // run while the products execute); keep the stages apart: hoisting every
+    // tile's reads and products to the top would hold all their registers
+    __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);   // LDS reads
+    __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);   // matrix products
+    __builtin_amdgcn_sched_group_barrier(0x002, 40, 0);  // vector ALU
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float sc = (kFused && i >= 2) ? sc1_prev : sc0_prev;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) acc[i][NA - 1][v] = __builtin_fmaf(p_prev[i][v], sc, acc[i][NA - 1][v]);
+  }
+}
+
+template <int MODE, class C>
+__global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void grouped_gemm_kernel(
     const uint8_t* __restrict__ aq, const float* __restrict__ as, const int* __restrict__ a_row, int a_rows,
     const uint8_t* __restrict__ bq, const float* __restrict__ bs, const int* __restrict__ offsets, int G,
     int N, int K, int n_tiles, int wg_per_xcd, void* __restrict__ out, float* __restrict__ hs_out) {
   constexpr bool kFused = MODE == OUT_SWIGLU;
+  constexpr int kThreads = C::kThreads, kBM = C::kBM, kWM = C::kWM, kTM = C::kTM, kStages = C::kStages;
+  constexpr int kStageBytes = C::kStageBytes, kOffA = C::kOffA, kOffB = C::kOffB, kOffS = C::kOffS;
+  constexpr int kSB = C::kSB, kWOps = C::kWOps, kAHi = C::kAHi, kNHi = C::kNHi, kGPT = C::kGPT;
   __shared__ __attribute__((aligned(1024))) uint8_t ring[kStages * kStageBytes];
   __shared__ int2 sTile[kMaxTilesPerWG];  // {g | n_tile << 10 | rows_valid << 21, row0}
 
@@ -105,11 +202,11 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
     int* sP = reinterpret_cast<int*>(ring);  // [G + 1] m-tile prefix
     int* sOff = sP + (kMaxGroups + 1);       // [G + 1] row offsets
     int* sScan = sOff + (kMaxGroups + 1);    // [kThreads]
-    int mt[2];
+    int mt[kGPT];
     int local = 0;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int g = tid * 2 + i;
+    for (int i = 0; i < kGPT; ++i) {
+      const int g = tid * kGPT + i;
       mt[i] = 0;
       if (g < G) {
         const int o0 = offsets[g], o1 = offsets[g + 1];
@@ -129,8 +226,8 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
     }
     int run = sScan[tid] - local;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int g = tid * 2 + i;
+    for (int i = 0; i < kGPT; ++i) {
+      const int g = tid * kGPT + i;
       if (g < G) sP[g] = run;
       run += mt[i];
     }
@@ -166,16 +263,17 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
   const int p16 = lane & 7;   // physical 16-byte piece inside the LDS row
   const int rsub = lane >> 3;  // row inside the 8-row (1 KB) DMA slice
   const int c16 = p16 ^ rsub;  // logical piece it must fetch (swizzle)
-  // activation slices (8 rows each): waves 0-3 take 3, waves 4-7 take 2; the
-  // scale load of waves 4-7 fills S: S[t] = sa of token t (t < 192, rows
-  // past the group clamped), S[192] / S[193] = weight-block scales A / B
-  const bool a3 = w < 4;
-  const int a_slice0 = a3 ? 3 * w : 12 + 2 * (w - 4);
+  // activation slices (8 rows each): waves [0, kNHi) take kAHi, the others
+  // kAHi - 1 and one scale load (see TileCfg)
+  const bool a_hi = w < kNHi;
+  const int a_slice0 = a_hi ? kAHi * w : kAHi * kNHi + (kAHi - 1) * (w - kNHi);
+  const int s_op = a_hi ? 0 : (w - kNHi) % C::kNScaleOps;  // scale load of this wave
+  const bool s_weight = s_op == C::kNScaleOps - 1;          // ... the weight-block scales
   const uint8_t* ia_base = aq;  // scalar bases of the tile being issued
   const uint8_t* ib_base = bq;
   const uint8_t* is_base = reinterpret_cast<const uint8_t*>(as);
-  uint32_t ia_off[3], ib_off[4], is_off = 0;  // per-lane byte offsets from them
-  int it = 0, ikb = 0;                         // next chunk to issue: tile it, chunk ikb
+  uint32_t ia_off[kAHi], ib_off[kWOps], is_off = 0;  // per-lane byte offsets from them
+  int it = 0, ikb = 0;                                // next chunk to issue: tile it, chunk ikb
   auto load_issue_tile = [&](int i) {
     const int2 e = sTile[i];
     const int wd = __builtin_amdgcn_readfirstlane(e.x);
@@ -187,32 +285,34 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
     if (a_row != nullptr) {
       ia_base = aq;
 #pragma unroll
-      for (int j = 0; j < 3; ++j) {
+      for (int j = 0; j < kAHi; ++j) {
         const int src = min(max(a_row[row0 + min((a_slice0 + j) * 8 + rsub, rows_valid - 1)], 0), a_rows - 1);
         ia_off[j] = (uint32_t)src * (uint32_t)K + (uint32_t)(c16 * 16);
       }
     } else {
       ia_base = aq + (int64_t)row0 * K;
 #pragma unroll
-      for (int j = 0; j < 3; ++j)
+      for (int j = 0; j < kAHi; ++j)
         ia_off[j] = (uint32_t)(min((a_slice0 + j) * 8 + rsub, rows_valid - 1) * K + c16 * 16);
     }
     const uint8_t* bq_g = bq + (int64_t)g * N * K;
     if (kFused) {
-      // waves 0-3 fetch gate block n_tile, waves 4-7 the matching up block
-      ib_base = bq_g + (int64_t)((w < 4 ? 0 : I) + n_tile * 128) * K;
+      // weight slices 0..15 hold gate block n_tile, 16..31 the matching up
+      // block; a wave's slices lie in one half
+      const int half = (w * kWOps) / 16;
+      ib_base = bq_g + (int64_t)((half ? I : 0) + n_tile * 128) * K;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) ib_off[j] = (uint32_t)((((w & 3) * 4 + j) * 8 + rsub) * K + c16 * 16);
+      for (int j = 0; j < kWOps; ++j) ib_off[j] = (uint32_t)((((w * kWOps + j) % 16) * 8 + rsub) * K + c16 * 16);
     } else {
       ib_base = bq_g + (int64_t)n_tile * kBN * K;
       const int last = N - 1 - n_tile * kBN;  // rows past N (a half tile) re-read row N - 1
 #pragma unroll
-      for (int j = 0; j < 4; ++j) ib_off[j] = (uint32_t)(min((w * 4 + j) * 8 + rsub, last) * K + c16 * 16);
+      for (int j = 0; j < kWOps; ++j) ib_off[j] = (uint32_t)(min((w * kWOps + j) * 8 + rsub, last) * K + c16 * 16);
     }
-    if (w < 4) {
+    if (a_hi) {
       // no scale load
-    } else if (w < 7) {
-      const int t = min((w - 4) * 64 + lane, rows_valid - 1);
+    } else if (!s_weight) {
+      const int t = min(s_op * 64 + lane, rows_valid - 1);
       if (a_row != nullptr) {
         is_base = reinterpret_cast<const uint8_t*>(as);
         is_off = (uint32_t)min(max(a_row[row0 + t], 0), a_rows - 1) * (uint32_t)(KB * 4);
@@ -229,16 +329,16 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
   };
   // Enqueue chunk (it, ikb) into the stage at LDS address `st`, then advance;
   // past the last chunk the last chunk is re-fetched, so every call issues
-  // exactly kDmaPerChunk loads per wave.
+  // exactly kDma loads per wave.
   auto issue_next = [&](uint32_t st) {
     const uint8_t* a = ia_base + ikb * 128;
     const uint8_t* b = ib_base + ikb * 128;
-    dma16(a, ia_off[0], st + kOffA + a_slice0 * 1024);
-    dma16(a, ia_off[1], st + kOffA + (a_slice0 + 1) * 1024);
-    if (a3) dma16(a, ia_off[2], st + kOffA + (a_slice0 + 2) * 1024);
-    else dma4(is_base + ikb * 4, is_off, st + kOffS + (w - 4) * 256);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(b, ib_off[j], st + kOffB + (w * 4 + j) * 1024);
+    for (int j = 0; j < kAHi - 1; ++j) dma16(a, ia_off[j], st + kOffA + (a_slice0 + j) * 1024);
+    if (a_hi) dma16(a, ia_off[kAHi - 1], st + kOffA + (a_slice0 + kAHi - 1) * 1024);
+    else dma4(is_base + ikb * 4, is_off, st + kOffS + s_op * 256);
+#pragma unroll
+    for (int j = 0; j < kWOps; ++j) dma16(b, ib_off[j], st + kOffB + (w * kWOps + j) * 1024);
     if (ikb + 1 < KB) {
       ++ikb;
     } else if (it + 1 < n_my) {
@@ -253,13 +353,13 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
   const uint32_t lane_hi = lane_lo ^ 16;
   // first weight row of instruction tile i (rows 16 i' + lane % 16)
   auto brow0 = [&](int i) { return kFused ? (i < 2 ? 0 : 128) + 32 * wn + 16 * (i & 1) : 64 * wn + 16 * i; };
-  const int sb_sel = kFused ? 0 : (wn >> 1);  // unfused: rows of waves 0,1 in block A, 2,3 in B
+  const int sb_sel = kFused ? 0 : (wn >> 1);  // unfused: rows of row-waves 0,1 in block A, 2,3 in B
 
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(ring));
   load_issue_tile(0);
-  issue_next(ring_lds);
-  issue_next(ring_lds + kStageBytes);
-  int ist = 2, cst = 0;  // stage receiving the next issue / holding the next chunk to multiply
+#pragma unroll
+  for (int s = 0; s < kStages - 1; ++s) issue_next(ring_lds + s * kStageBytes);
+  int ist = kStages - 1, cst = 0;  // stage receiving the next issue / holding the next chunk to multiply
 
   for (int ti = 0; ti < n_my; ++ti) {
     const int2 e = sTile[ti];
@@ -280,11 +380,11 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
 
     const uint8_t* st = ring;
     for (int kb = 0; kb < KB; ++kb) {
-      // this wave's loads of the chunk in stage cst have landed (only the next
-      // chunk's may still fly; loads complete in issue order) ...
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(kDmaPerChunk));
+      // this wave's loads of the chunk in stage cst have landed (only the
+      // later chunks' may still fly; loads complete in issue order) ...
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm((kStages - 2) * C::kDma));
       // ... and every other wave's too; all waves are also done with the
-      // previous chunk, whose stage receives the chunk after next now
+      // previous chunk, whose stage receives the chunk kStages - 1 ahead now
       __builtin_amdgcn_s_barrier();
       issue_next(ring_lds + ist * kStageBytes);
       ist = ist == kStages - 1 ? 0 : ist + 1;
@@ -297,25 +397,12 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
       for (int i = 0; i < 4; ++i) a_op[i] = lds_operand(st + kOffB + brow0(i) * 128, lane_lo, lane_hi);
       const float sb0 = kFused ? sS[kSB] : sS[kSB + sb_sel];
       const float sb1 = kFused ? sS[kSB + 1] : sb0;
-      // active tiles are a prefix (j < n_active): leaving at the first
-      // inactive one gives the compiler one nested region to schedule
-#pragma unroll
-      for (int j = 0; j < kTM; ++j) {
-        if (j >= n_active) break;
-        const v8i b_op = lds_operand(st + kOffA + (wm * kWM + 16 * j) * 128, lane_lo, lane_hi);
-        const float sa = sS[wm * kWM + 16 * j + l16];
-        const float sc0 = sa * sb0;
-        const float sc1 = kFused ? sa * sb1 : sc0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const v4f p = mfma_chunk(a_op[i], b_op);
-          const float sc = (kFused && i >= 2) ? sc1 : sc0;
-          acc[i][j][0] = __builtin_fmaf(p[0], sc, acc[i][j][0]);
-          acc[i][j][1] = __builtin_fmaf(p[1], sc, acc[i][j][1]);
-          acc[i][j][2] = __builtin_fmaf(p[2], sc, acc[i][j][2]);
-          acc[i][j][3] = __builtin_fmaf(p[3], sc, acc[i][j][3]);
-        }
-      }
+      // every instruction tile of the wave, active or not (a ragged tile's
+      // inactive ones hold clamped copies of its last row and are never
+      // stored): one straight-line, software-pipelined body
+      if (n_active > 0)
+        mma_chunk<kTM, kFused, kTM>(acc, a_op, st + kOffA + wm * kWM * 128, sS + wm * kWM, sb0, sb1, lane_lo,
+                                    lane_hi, l16);
     }
 
     // ---- epilogue (the next tile's first chunks keep streaming in) ----
@@ -387,28 +474,27 @@ __global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
-// Compute units of the current device (cached per device).
+// Compute units of the current device (looked up once per device; the
+// stored value is the same whichever thread stores it).
 int device_cu_count() {
-  static int cache[64];
+  static std::atomic<int> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cache[dev] == 0) {
-    int n = 0;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
     if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev] = n;
+    cache[dev].store(n, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return n;
 }
 
-template <int MODE>
-moe_status launch_gemm(const uint8_t* aq, const float* as, const int* a_row, int64_t a_rows,
-                       const uint8_t* bq, const float* bs, const int* offsets, int G, int64_t M, int N,
-                       int K, void* out, float* hs, hipStream_t st, const char* what) {
-  const int n_tiles = MODE == OUT_SWIGLU ? (N / 2) / 128 : (N + kBN - 1) / kBN;
-  if (n_tiles > kMaxNTiles) return fail(MOE_ERR_UNSUPPORTED, "%s: N=%d too large", what, N);
+template <int MODE, class C>
+moe_status launch_cfg(const uint8_t* aq, const float* as, const int* a_row, int64_t a_rows, const uint8_t* bq,
+                      const float* bs, const int* offsets, int G, int64_t M, int N, int K, int n_tiles, void* out,
+                      float* hs, hipStream_t st, const char* what) {
   // Upper bound on the m-tiles: sum_g ceil(M_g / BM) <= floor(M / BM) + G, and
   // every m-tile holds at least one row.
-  int64_t mt_bound = M / kBM + G;
+  int64_t mt_bound = M / C::kBM + G;
   if (mt_bound > M) mt_bound = M;
   const int64_t tiles = mt_bound * n_tiles;
   if (tiles == 0) return MOE_OK;
@@ -426,9 +512,22 @@ moe_status launch_gemm(const uint8_t* aq, const float* as, const int* a_row, int
     if (wg_per_xcd < need) wg_per_xcd = need;
     if (wg_per_xcd > per_xcd) wg_per_xcd = per_xcd;
   }
-  grouped_gemm_kernel<MODE><<<(unsigned)(8 * wg_per_xcd), kThreads, 0, st>>>(
+  // every workgroup's share of its XCD's tiles fits its tile list (the
+  // kernel would otherwise drop the excess)
+  if ((per_xcd + wg_per_xcd - 1) / wg_per_xcd > kMaxTilesPerWG)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: tile list overflow", what);
+  grouped_gemm_kernel<MODE, C><<<(unsigned)(8 * wg_per_xcd), C::kThreads, 0, st>>>(
       aq, as, a_row, (int)a_rows, bq, bs, offsets, G, N, K, n_tiles, (int)wg_per_xcd, out, hs);
   return after_launch(what, st);
+}
+
+template <int MODE>
+moe_status launch_gemm(const uint8_t* aq, const float* as, const int* a_row, int64_t a_rows,
+                       const uint8_t* bq, const float* bs, const int* offsets, int G, int64_t M, int N,
+                       int K, void* out, float* hs, hipStream_t st, const char* what) {
+  const int n_tiles = MODE == OUT_SWIGLU ? (N / 2) / 128 : (N + kBN - 1) / kBN;
+  if (n_tiles > kMaxNTiles) return fail(MOE_ERR_UNSUPPORTED, "%s: N=%d too large", what, N);
+  return launch_cfg<MODE, CfgS>(aq, as, a_row, a_rows, bq, bs, offsets, G, M, N, K, n_tiles, out, hs, st, what);
 }
 
 moe_status check_gemm_args(const uint8_t* aq, const float* as, const int32_t* a_row, int64_t a_rows,

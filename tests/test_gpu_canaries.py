@@ -54,14 +54,16 @@ def _gemm_operands(sizes, N, K):
 
 
 SIZES = [5, 0, 17, 1, 300, 161, 0, 33]
+LARGE = [1000, 0, 700, 3]          # several full m-tiles per group
 
 
+@pytest.mark.parametrize("sizes", [SIZES, LARGE])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 @pytest.mark.parametrize("N,K", [(384, 256), (256, 4224)])
-def test_gemm_output_bands(dtype, N, K):
+def test_gemm_output_bands(sizes, dtype, N, K):
     """N = 384: the last 256-row weight tile is half past N; K = 4224: one
     tile per workgroup (above the persistent walk's limit)."""
-    args, M = _gemm_operands(SIZES, N, K)
+    args, M = _gemm_operands(sizes, N, K)
     _all_written({"c": ((M, N), dtype)}, lambda o: R.grouped_gemm_fp8_blockscaled(*args, c=o["c"]))
     perm = RNG.permutation(M).astype(np.int32)
     src_q, src_s = torch.empty_like(args[0]), torch.empty_like(args[1])
@@ -71,10 +73,11 @@ def test_gemm_output_bands(dtype, N, K):
         src_q, src_s, to_dev(perm), *args[2:], c=o["c"]))
 
 
+@pytest.mark.parametrize("sizes", [SIZES, LARGE])
 @pytest.mark.parametrize("K", [256, 4224])
-def test_fused_swiglu_output_bands(K):
+def test_fused_swiglu_output_bands(sizes, K):
     I = 384
-    args, M = _gemm_operands(SIZES, 2 * I, K)
+    args, M = _gemm_operands(sizes, 2 * I, K)
     _all_written({"hq": ((M, I), torch.uint8), "hs": ((M, I // 128), torch.float32)},
                  lambda o: R.grouped_gemm_fp8_swiglu(*args, hq=o["hq"], hs=o["hs"]))
     c1 = R.grouped_gemm_fp8_blockscaled(*args)

@@ -439,3 +439,36 @@ def test_combine(T, K, H, shared):
     far = d > 1
     assert np.all(np.abs(got - ref)[far] <= ulp[far] + (2 * K + 1) * 2.0 ** -24 * mag[far])
     assert far.mean() < 1e-3
+
+
+@pytest.mark.parametrize("K", [640, 4224])
+def test_grouped_gemm_large_groups(K):
+    """Groups of hundreds of rows, several m-tiles each (K = 640: the
+    persistent tile walk; K = 4224: one tile per workgroup): ragged groups
+    (a 3-row one, an empty one), a half weight tile (N = 384), against the
+    oracle; bf16 output equal to the rounded float32 output; row gather;
+    the fused SwiGLU equal to the unfused GEMM + SwiGLU."""
+    sizes = [1000, 0, 700, 3]
+    aq, as_, bq, bs, off = _gemm_problem(sizes, 384, K, RNG)
+    args = [to_dev(v) for v in (aq, as_, bq, bs, off)]
+    c = R.grouped_gemm_fp8_blockscaled(*args)
+    C, Mag = O.grouped_gemm(aq, as_, bq, bs, off)
+    assert_gemm_close(np_(c), C, Mag, what=f"large groups K={K}")
+    c16 = R.grouped_gemm_fp8_blockscaled(*args, out_dtype=torch.bfloat16)
+    assert np.array_equal(bf16_bits(c16), bf16_bits(c.to(torch.bfloat16)))
+    M = int(off[-1])
+    perm = RNG.permutation(M)
+    src_q, src_s = np.empty_like(aq), np.empty_like(as_)
+    src_q[perm], src_s[perm] = aq, as_
+    cg = R.grouped_gemm_fp8_blockscaled_gather(to_dev(src_q), to_dev(src_s), to_dev(perm.astype(np.int32)),
+                                               *args[2:])
+    assert torch.equal(cg, c)
+    I = 256
+    aq2, as2, bq2, bs2, off2 = _gemm_problem([900, 5, 700], 2 * I, K, RNG)
+    args2 = [to_dev(v) for v in (aq2, as2, bq2, bs2, off2)]
+    hq, hs = R.grouped_gemm_fp8_swiglu(*args2)
+    c1 = R.grouped_gemm_fp8_blockscaled(*args2)
+    hq2, hs2 = R.swiglu(c1)
+    assert torch.equal(hq, hq2) and torch.equal(hs, hs2)
+    C1, Mag1 = O.grouped_gemm(aq2, as2, bq2, bs2, off2)
+    assert_gemm_close(np_(c1), C1, Mag1, what=f"large groups gate|up K={K}")
