@@ -283,6 +283,35 @@ def router_rows(cfg, d, fwd, torch, R, synth, reps=5):
                 bias_update_us=ms_b * 1e3)
 
 
+def fusion_rows(cfg, d, w, torch, R, reps=20):
+    """The layer forward with the single-launch routing + permutation
+    (moe_route_permute) and the combine fused into the down projection
+    (grouped_gemm_fp8_combine), each on and off, on the timed workload: the
+    layer time of every combination (y is bit-identical in all four) and the
+    stage times of the two extremes."""
+    T, H, E, I = cfg["T"], cfg["H"], cfg["E"], cfg["I"]
+    dev = d["x"].device
+    out = {}
+    ref = None
+    for frp in (False, True):
+        for fc in (False, True):
+            f = R.MoEForward(T, H, E, I, cfg["route"], w, dev, fused=True, shared_I=cfg.get("shared_I"),
+                             fuse_route_permute=frp, fuse_combine=fc)
+            y = f(d["x"], d["logits"], d["bias"])
+            torch.cuda.synchronize()
+            same = True if ref is None else bool(torch.equal(y.view(torch.int16), ref))
+            if ref is None:
+                ref = y.view(torch.int16).clone()
+            ms = time_op(lambda: f(d["x"], d["logits"], d["bias"]), reps, torch)
+            row = dict(layer_ms=ms, y_bit_identical=same)
+            if frp == fc:
+                _, st = staged(lambda m: f(d["x"], d["logits"], d["bias"], on_stage=m), 5, torch)
+                row["stage_ms"] = st
+            out[f"route_permute_{'fused' if frp else 'separate'}__combine_{'fused' if fc else 'separate'}"] = row
+            del f
+    return out
+
+
 def graph_rows(torch, R, synth, reps=50):
     """The layer forward eager vs replayed from a captured HIP graph on the
     small layers, where kernel launches, not the kernels, set the step time:
@@ -750,6 +779,8 @@ def main():
         extra["router"] = router_rows(cfg, d, fwd, torch, R, synth)
         log("input-side backward")
         extra["backward"] = backward_rows(cfg, d, w, torch, R, synth)
+        log("fused stages on and off")
+        extra["stage_fusions"] = fusion_rows(cfg, d, w, torch, R)
         log("small layer: eager vs HIP graph replay")
         extra["graph"] = graph_rows(torch, R, synth)
         log("other workloads: MoGE and skewed-load layers")

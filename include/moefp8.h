@@ -184,6 +184,44 @@ MOE_API moe_status moe_permute_noalloc(const int32_t* topk_idx, int32_t T, int32
                                uint8_t* aq, float* as, void* stream);
 
 /*
+ * moe_route_permute_workspace_size -- bytes of device workspace
+ * moe_route_permute needs for (T, K, E).  Host-only.
+ */
+MOE_API moe_status moe_route_permute_workspace_size(int32_t T, int32_t K, int32_t E, size_t* bytes);
+
+/*
+ * moe_route_permute -- moe_route and the index maps of moe_permute in one
+ * launch.                      [DSV3-MOE], [PANGU-MOGE]; operator fusion of
+ *                              the Pangu page's system optimisation section
+ *
+ * Arguments as moe_route (logits .. topk_gate) and moe_permute's index maps
+ * (expert_offsets, dst_row, src_token); the results are identical, bit for
+ * bit, to moe_route followed by moe_permute with xq == NULL.  The
+ * permutation's counting runs inside the routing workgroups and the ranking
+ * workgroups wait (bounded) for the last routing workgroup's scan, so no
+ * host or stream synchronisation separates the stages.
+ *
+ *  workspace  >= moe_route_permute_workspace_size(T, K, E) bytes, 16-B
+ *             aligned.  Its first 256 bytes are counters kept between calls:
+ *             ZERO-FILL them before the first use (e.g. hipMemset once after
+ *             allocation); every call that completes leaves them zero again,
+ *             so one workspace serves calls of any shapes it is large enough
+ *             for.  The rest is scratch, written before it is read.  Calls
+ *             that share a workspace must not overlap (same stream, or
+ *             serialised).  Word 4 (int32) counts ranking workgroups whose
+ *             wait ran out (never, with zeroed counters; such a workgroup
+ *             writes nothing); it is never cleared by the library.
+ *  With T == 0 only expert_offsets (all zeros) and the workspace are used.
+ * Errors: as moe_route and moe_permute (MOE_ERR_WORKSPACE when the workspace
+ *         is too small).
+ */
+MOE_API moe_status moe_route_permute(const float* logits, const float* bias, int32_t T, int32_t E, int32_t K,
+                             int32_t n_groups, int32_t k_per_group, moe_route_mode mode,
+                             int32_t normalize_topk, int32_t* topk_idx, float* topk_gate,
+                             int32_t* expert_offsets, int32_t* dst_row, int32_t* src_token,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * quant_act_1x128_e4m3 -- per-(row, 128-column tile) FP8 quantisation of
  * activations.                                        [KANANA-FP8], [DSV3-FP8]
  *
@@ -323,6 +361,50 @@ MOE_API moe_status swiglu(const float* gate_up, int64_t M, int32_t I, uint8_t* h
 MOE_API moe_status moe_combine(const float* y_perm, const int32_t* dst_row, const float* topk_gate,
                        const float* shared, int32_t T, int32_t K, int32_t H, uint16_t* out_bf16,
                        void* stream);
+
+/*
+ * grouped_gemm_fp8_combine_workspace_size -- bytes of the arrival counters
+ * grouped_gemm_fp8_combine needs for T tokens and N output columns.
+ * Host-only.
+ */
+MOE_API moe_status grouped_gemm_fp8_combine_workspace_size(int32_t T, int32_t N, size_t* bytes);
+
+/*
+ * grouped_gemm_fp8_combine -- the down projection with moe_combine fused into
+ * its epilogue.            [DSV3-FP8], [DSV3-MOE]; operator fusion of the
+ *                          Pangu page's system optimisation section
+ *
+ * Writes c exactly as grouped_gemm_fp8_blockscaled(aq, as, bq, bs,
+ * group_offsets, G, M, N, K, c, MOE_F32) and y exactly as
+ * moe_combine(c, dst_row, topk_gate, shared, T, topk, N, y_bf16), bit for
+ * bit, in one launch: the workgroup tile that finishes last among the topk
+ * tiles holding a token's rows (per 256-column slice; an arrival counter
+ * elects it) sums them in slot order.  The election never changes the order
+ * of the sum, so y does not depend on scheduling.
+ *
+ *  aq .. K, c   as grouped_gemm_fp8_blockscaled with c f32 [M, N] (out)
+ *  src_token    i32 [M]        token of grouped row m       (moe_permute)
+ *  dst_row      i32 [T, topk]  grouped row of (t, k)        (moe_permute)
+ *  topk_gate    f32 [T, topk]                               (moe_route)
+ *  shared       f32 [T, N] or NULL; must be complete when the launch starts
+ *  y_bf16       u16 [T, N] (out) bf16 bit patterns
+ *  counters     >= grouped_gemm_fp8_combine_workspace_size(T, N) bytes,
+ *               ZERO-FILLED before the first use (e.g. hipMemset once after
+ *               allocation); every call that completes leaves them zero.
+ *               Calls sharing counters must not overlap.
+ *  M == T * topk (no token dropped); src_token and dst_row must be a
+ *  permutation and its inverse, as moe_permute writes them (otherwise y is
+ *  unspecified and the counters may be left non-zero; no access leaves the
+ *  buffers).
+ * Errors: as grouped_gemm_fp8_blockscaled; MOE_ERR_SHAPE (M != T * topk),
+ *         MOE_ERR_WORKSPACE (counters too small).
+ */
+MOE_API moe_status grouped_gemm_fp8_combine(const uint8_t* aq, const float* as, const uint8_t* bq,
+                                    const float* bs, const int32_t* group_offsets, int32_t G, int64_t M,
+                                    int32_t N, int32_t K, float* c, const int32_t* src_token,
+                                    const int32_t* dst_row, const float* topk_gate, const float* shared,
+                                    int32_t T, int32_t topk, uint16_t* y_bf16, int32_t* counters,
+                                    size_t counters_bytes, void* stream);
 
 /*
  * fp8_block_transpose -- transpose of block-quantised weights, codes and

@@ -8,7 +8,8 @@ fails loudly if the library has not been built.
 
 from ._lib import (MoeError, fp8_block_transpose, grouped_gemm_fp8_blockscaled,
                    grouped_gemm_fp8_blockscaled_gather, quant_weight_128x128_e4m3_t, moe_sigmoid_f32,
-                   moe_permute_noalloc,
+                   moe_permute_noalloc, moe_route_permute, moe_route_permute_workspace_size,
+                   grouped_gemm_fp8_combine, grouped_gemm_fp8_combine_workspace_size,
                    grouped_gemm_fp8_swiglu, moe_combine, moe_combine_backward, moe_permute,
                    moe_permute_workspace_size, moe_route, moe_route_backward, quant_act_1x128_e4m3,
                    quant_weight_128x128_e4m3, swiglu, swiglu_backward, moe_wgrad_padded_rows,
@@ -18,7 +19,8 @@ from .layer import MoEBackward, MoEForward, MoEWeightGrad, quantize_weights, tra
 
 __all__ = ["MoeError", "fp8_block_transpose", "grouped_gemm_fp8_blockscaled",
            "grouped_gemm_fp8_blockscaled_gather", "quant_weight_128x128_e4m3_t", "moe_sigmoid_f32",
-           "moe_permute_noalloc",
+           "moe_permute_noalloc", "moe_route_permute", "moe_route_permute_workspace_size",
+           "grouped_gemm_fp8_combine", "grouped_gemm_fp8_combine_workspace_size",
            "grouped_gemm_fp8_swiglu", "moe_combine", "moe_permute", "moe_permute_workspace_size",
            "moe_route", "quant_act_1x128_e4m3", "quant_weight_128x128_e4m3", "swiglu",
            "moe_combine_backward", "swiglu_backward", "moe_route_backward",

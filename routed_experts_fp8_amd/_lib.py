@@ -28,6 +28,9 @@ _SIGNATURES = {
     "moe_permute_workspace_size": (_i32, [_i32, _i32, _i32, ctypes.POINTER(_sz)]),
     "moe_permute": (_i32, [_c_void_p, _i32, _i32, _i32, _c_void_p, _c_void_p, _i32, _c_void_p,
                            _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p]),
+    "moe_route_permute_workspace_size": (_i32, [_i32, _i32, _i32, ctypes.POINTER(_sz)]),
+    "moe_route_permute": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _c_void_p,
+                                 _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _sz, _c_void_p]),
     "moe_permute_noalloc": (_i32, [_c_void_p, _i32, _i32, _i32, _c_void_p, _c_void_p, _i32, _c_void_p,
                                    _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p]),
     "quant_act_1x128_e4m3": (_i32, [_c_void_p, _i32, _i64, _i32, _c_void_p, _c_void_p, _c_void_p]),
@@ -42,6 +45,10 @@ _SIGNATURES = {
                                                    _i32, _c_void_p]),
     "grouped_gemm_fp8_swiglu": (_i32, [_c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p, _c_void_p,
                                        _c_void_p, _i32, _i64, _i32, _i32, _c_void_p, _c_void_p, _c_void_p]),
+    "grouped_gemm_fp8_combine_workspace_size": (_i32, [_i32, _i32, ctypes.POINTER(_sz)]),
+    "grouped_gemm_fp8_combine": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i64, _i32,
+                                        _i32, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32,
+                                        _c_void_p, _c_void_p, _sz, _c_void_p]),
     "swiglu": (_i32, [_c_void_p, _i64, _i32, _c_void_p, _c_void_p, _c_void_p]),
     "moe_combine": (_i32, [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i32, _i32, _c_void_p,
                            _c_void_p]),
@@ -227,6 +234,46 @@ def moe_permute_noalloc(topk_idx, E, xq=None, xs=None, out=None):
     return res
 
 
+def moe_route_permute_workspace_size(T, K, E):
+    n = _sz(0)
+    _check("moe_route_permute_workspace_size", lib.moe_route_permute_workspace_size(T, K, E, ctypes.byref(n)))
+    return n.value
+
+
+def moe_route_permute(logits, bias, K, mode="sigmoid_bias", n_groups=1, k_per_group=None, normalize=True,
+                      workspace=None, out=None):
+    """moe_route and moe_permute's index maps in one launch -> dict(topk_idx,
+    topk_gate, offsets, dst_row, src_token).  The first 256 bytes of
+    ``workspace`` (uint8) must be zero before its first use (every call
+    leaves them zero); without one a zero-filled workspace is allocated for
+    this call."""
+    _need(logits, "logits", torch.float32)
+    T, E = logits.shape
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (E,))
+    m = ROUTE_SIGMOID_BIAS if mode == "sigmoid_bias" else ROUTE_SOFTMAX_GROUPED
+    if m == ROUTE_SOFTMAX_GROUPED:
+        k_per_group = K // n_groups if k_per_group is None else k_per_group
+        normalize = False
+    dev = logits.device
+    out = dict(out or {})
+    res = {
+        "topk_idx": _out(out.get("topk_idx"), "topk_idx", (T, K), torch.int32, dev),
+        "topk_gate": _out(out.get("topk_gate"), "topk_gate", (T, K), torch.float32, dev),
+        "offsets": _out(out.get("offsets"), "offsets", (E + 1,), torch.int32, dev),
+        "dst_row": _out(out.get("dst_row"), "dst_row", (T, K), torch.int32, dev),
+        "src_token": _out(out.get("src_token"), "src_token", (T * K,), torch.int32, dev),
+    }
+    if workspace is None:
+        workspace = torch.zeros(moe_route_permute_workspace_size(T, K, E), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8)
+    _check("moe_route_permute", lib.moe_route_permute(
+        _p(logits), _p(bias), T, E, K, n_groups, k_per_group or K, m, int(bool(normalize)), _p(res["topk_idx"]),
+        _p(res["topk_gate"]), _p(res["offsets"]), _p(res["dst_row"]), _p(res["src_token"]), _p(workspace),
+        workspace.numel(), _stream()))
+    return res
+
+
 def quant_act_1x128_e4m3(x, q=None, scale=None):
     """x float32/bf16 [rows, cols] -> (codes uint8 [rows, cols], scales f32 [rows, cols/128])."""
     code = _dtype_code(x)
@@ -324,6 +371,39 @@ def grouped_gemm_fp8_swiglu(aq, as_, bq, bs, offsets, hq=None, hs=None, a_row=No
     _check("grouped_gemm_fp8_swiglu", lib.grouped_gemm_fp8_swiglu(
         _p(aq), _p(as_), _p(a_row), A, _p(bq), _p(bs), _p(offsets), G, M, I, K, _p(hq), _p(hs), _stream()))
     return hq, hs
+
+
+def grouped_gemm_fp8_combine_workspace_size(T, N):
+    n = _sz(0)
+    _check("grouped_gemm_fp8_combine_workspace_size",
+           lib.grouped_gemm_fp8_combine_workspace_size(T, N, ctypes.byref(n)))
+    return n.value
+
+
+def grouped_gemm_fp8_combine(aq, as_, bq, bs, offsets, src_token, dst_row, topk_gate, shared=None, c=None,
+                             y=None, counters=None):
+    """The down projection with the combine fused into its epilogue ->
+    (c f32 [M, N], y bf16 [T, N]), both identical to grouped_gemm_fp8_blockscaled
+    followed by moe_combine.  ``counters`` (int32) must have been zero-filled
+    before its first use (every call leaves it zero-filled); without it a
+    zero-filled one is allocated for this call."""
+    M, K, G, N, A = _gemm_operands(aq, as_, bq, bs, offsets, None)
+    _need(dst_row, "dst_row", torch.int32)
+    T, topk = dst_row.shape
+    _need(src_token, "src_token", torch.int32, (M,))
+    _need(topk_gate, "topk_gate", torch.float32, (T, topk))
+    if shared is not None:
+        _need(shared, "shared", torch.float32, (T, N))
+    c = _out(c, "c", (M, N), torch.float32, aq.device)
+    y = _out(y, "y", (T, N), torch.bfloat16, aq.device)
+    need = grouped_gemm_fp8_combine_workspace_size(T, N)
+    if counters is None:
+        counters = torch.zeros(max(need // 4, 1), dtype=torch.int32, device=aq.device)
+    _need(counters, "counters", torch.int32)
+    _check("grouped_gemm_fp8_combine", lib.grouped_gemm_fp8_combine(
+        _p(aq), _p(as_), _p(bq), _p(bs), _p(offsets), G, M, N, K, _p(c), _p(src_token), _p(dst_row),
+        _p(topk_gate), _p(shared), T, topk, _p(y), _p(counters), counters.numel() * 4, _stream()))
+    return c, y
 
 
 def swiglu(gate_up, hq=None, hs=None):

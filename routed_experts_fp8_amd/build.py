@@ -27,7 +27,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["status.cpp", "quant.hip", "transpose.hip", "route.hip", "permute.hip",
+SOURCES = ["status.cpp", "quant.hip", "transpose.hip", "route.hip", "permute.hip", "route_permute.hip",
            "swiglu_combine.hip", "gemm.hip", "backward.hip", "wgrad.hip", "router.hip"]
 
 FLAGS = [

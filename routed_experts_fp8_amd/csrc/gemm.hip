@@ -71,7 +71,7 @@
 namespace moefp8 {
 namespace {
 
-enum { OUT_F32 = 0, OUT_BF16 = 1, OUT_SWIGLU = 2 };
+enum { OUT_F32 = 0, OUT_BF16 = 1, OUT_SWIGLU = 2, OUT_COMBINE = 3 };
 
 constexpr int kBN = 256;               // weight rows per workgroup tile (4 row-waves of 64)
 constexpr int kMaxGroups = 1024;
@@ -175,11 +175,127 @@ __device__ __forceinline__ void mma_chunk(v4f (&acc)[4][kTM], const v8i (&a_op)[
   }
 }
 
+// The gate-weighted combine fused into the down projection's epilogue
+// (OUT_COMBINE).  Each (token, n-tile) pair receives exactly topk grouped
+// rows, one per selected expert, computed by topk workgroup tiles in any
+// order.  A tile stores its float32 rows as usual, publishes them
+// device-wide, and bumps one arrival counter per row; the tile that brings a
+// counter to topk is the last one for that (token, n-tile), so every row it
+// needs is already written.  It sums the token's topk rows over its 256
+// columns in slot order, exactly as moe_combine does (the same binary32
+// operations in the same order), adds the shared expert's row, and writes y
+// in bf16.  The counter only elects who sums, never the order, so y is
+// reproducible bit for bit; the elected tile resets the counter to zero.
+struct CombineArgs {
+  const int* row_token;  // [M] token of grouped row m
+  const int* dst_row;    // [T, topk] grouped row of (token, slot)
+  const float* gate;     // [T, topk]
+  const float* shared;   // [T, N] or nullptr
+  uint16_t* y;           // [T, N] bf16 bits
+  int* counters;         // [T, n_tiles], zero between calls
+  int T, topk;
+  int64_t M;
+};
+
+// y[t, n_tile * 256 + 4 lane .. + 4] of one elected token (one wavefront).
+__device__ __forceinline__ void combine_token(const CombineArgs& cb, const float* c, int t, int col, int N) {
+  constexpr int kBatch = 8;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  const int* drow = cb.dst_row + (int64_t)t * cb.topk;
+  const float* grow = cb.gate + (int64_t)t * cb.topk;
+  for (int k0 = 0; k0 < cb.topk; k0 += kBatch) {
+    u32x4 v[kBatch];
+    float g[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (k0 + j < cb.topk) {
+        const int r = min(max(drow[k0 + j], 0), (int)cb.M - 1);
+        g[j] = grow[k0 + j];
+        v[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(c + (int64_t)r * N + col));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (k0 + j < cb.topk) {
+        acc[0] = acc[0] + g[j] * __uint_as_float(v[j][0]);
+        acc[1] = acc[1] + g[j] * __uint_as_float(v[j][1]);
+        acc[2] = acc[2] + g[j] * __uint_as_float(v[j][2]);
+        acc[3] = acc[3] + g[j] * __uint_as_float(v[j][3]);
+      }
+    }
+  }
+  if (cb.shared) {
+    const u32x4 s4 = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cb.shared + (int64_t)t * N + col));
+    acc[0] = acc[0] + __uint_as_float(s4[0]);
+    acc[1] = acc[1] + __uint_as_float(s4[1]);
+    acc[2] = acc[2] + __uint_as_float(s4[2]);
+    acc[3] = acc[3] + __uint_as_float(s4[3]);
+  }
+  uint2 o;
+  o.x = bf16_rne_bits(acc[0]) | (bf16_rne_bits(acc[1]) << 16);
+  o.y = bf16_rne_bits(acc[2]) | (bf16_rne_bits(acc[3]) << 16);
+  *reinterpret_cast<uint2*>(cb.y + (int64_t)t * N + col) = o;
+}
+
+// Called by every wave after the tile's rows are stored; `lds` is the ring
+// stage just multiplied (free until the next K step's barrier).  One
+// device-scope release and one acquire per tile, both in wave 0: every wave
+// first waits for its own stores, the workgroup barrier orders them before
+// wave 0's release, and the second barrier orders wave 0's acquire before
+// the other waves' loads.
+template <class C>
+__device__ __forceinline__ void combine_epilogue(const CombineArgs& cb, uint8_t* lds, const float* c, int row0,
+                                                 int rows_valid, int n_tile, int n_tiles, int N) {
+  constexpr int kRW = (C::kBM + 63) / 64;  // 64-row groups of the tile
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  int* sTok = reinterpret_cast<int*>(lds);  // [kRW][64] elected tokens
+  int* sCnt = sTok + kRW * 64;              // [kRW]
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));  // this wave's rows are written
+  __syncthreads();                           // ... every wave's; the stage is free
+  if (w == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // publish the tile's rows device-wide
+    uint64_t any = 0;
+#pragma unroll
+    for (int rw = 0; rw < kRW; ++rw) {
+      const int r = rw * 64 + lane;
+      int t = 0;
+      bool last = false;
+      if (r < rows_valid) {
+        t = cb.row_token[row0 + r];
+        if ((unsigned)t < (unsigned)cb.T) {
+          int* ctr = cb.counters + (int64_t)t * n_tiles + n_tile;
+          last = atomicAdd(ctr, 1) == cb.topk - 1;
+          if (last) __hip_atomic_store(ctr, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      const uint64_t m = __ballot(last);
+      if (last) sTok[rw * 64 + __popcll(m & ((1ull << lane) - 1ull))] = t;
+      if (lane == 0) sCnt[rw] = __popcll(m);
+      any |= m;
+    }
+    if (any) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other tiles' rows
+  }
+  __syncthreads();
+  const int col = n_tile * kBN + 4 * lane;
+  int j = 0;
+#pragma unroll
+  for (int rw = 0; rw < kRW; ++rw) {
+    const int cnt = __builtin_amdgcn_readfirstlane(sCnt[rw]);
+    for (int i = 0; i < cnt; ++i, ++j) {
+      if (j % C::kWaves != w) continue;
+      const int t = __builtin_amdgcn_readfirstlane(sTok[rw * 64 + i]);
+      if (col < N) combine_token(cb, c, t, col, N);
+    }
+  }
+}
+
 template <int MODE, class C>
 __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void grouped_gemm_kernel(
     const uint8_t* __restrict__ aq, const float* __restrict__ as, const int* __restrict__ a_row, int a_rows,
     const uint8_t* __restrict__ bq, const float* __restrict__ bs, const int* __restrict__ offsets, int G,
-    int N, int K, int n_tiles, int wg_per_xcd, void* __restrict__ out, float* __restrict__ hs_out) {
+    int N, int K, int n_tiles, int wg_per_xcd, void* __restrict__ out, float* __restrict__ hs_out,
+    CombineArgs cmb) {
   constexpr bool kFused = MODE == OUT_SWIGLU;
   constexpr int kThreads = C::kThreads, kBM = C::kBM, kWM = C::kWM, kTM = C::kTM, kStages = C::kStages;
   constexpr int kStageBytes = C::kStageBytes, kOffA = C::kOffA, kOffB = C::kOffB, kOffS = C::kOffS;
@@ -415,7 +531,7 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void grouped_gemm_kerne
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int n = n_tile * kBN + wn * 64 + 16 * i + 4 * q;
-            if (MODE == OUT_F32) {
+            if (MODE == OUT_F32 || MODE == OUT_COMBINE) {
               float4 v = make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
               *reinterpret_cast<float4*>(reinterpret_cast<float*>(out) + m * N + n) = v;
             } else {
@@ -427,6 +543,9 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void grouped_gemm_kerne
           }
         }
       }
+      if constexpr (MODE == OUT_COMBINE)
+        combine_epilogue<C>(cmb, const_cast<uint8_t*>(st), reinterpret_cast<const float*>(out), row0, rows_valid,
+                            n_tile, n_tiles, N);
     } else {
       // h = silu(g) * u into the gate accumulators; per-token amax over this
       // wave's 32 h columns, then across the 4 row-waves through LDS.  The
@@ -491,7 +610,7 @@ int device_cu_count() {
 template <int MODE, class C>
 moe_status launch_cfg(const uint8_t* aq, const float* as, const int* a_row, int64_t a_rows, const uint8_t* bq,
                       const float* bs, const int* offsets, int G, int64_t M, int N, int K, int n_tiles, void* out,
-                      float* hs, hipStream_t st, const char* what) {
+                      float* hs, const CombineArgs& cmb, hipStream_t st, const char* what) {
   // Upper bound on the m-tiles: sum_g ceil(M_g / BM) <= floor(M / BM) + G, and
   // every m-tile holds at least one row.
   int64_t mt_bound = M / C::kBM + G;
@@ -517,17 +636,19 @@ moe_status launch_cfg(const uint8_t* aq, const float* as, const int* a_row, int6
   if ((per_xcd + wg_per_xcd - 1) / wg_per_xcd > kMaxTilesPerWG)
     return fail(MOE_ERR_UNSUPPORTED, "%s: tile list overflow", what);
   grouped_gemm_kernel<MODE, C><<<(unsigned)(8 * wg_per_xcd), C::kThreads, 0, st>>>(
-      aq, as, a_row, (int)a_rows, bq, bs, offsets, G, N, K, n_tiles, (int)wg_per_xcd, out, hs);
+      aq, as, a_row, (int)a_rows, bq, bs, offsets, G, N, K, n_tiles, (int)wg_per_xcd, out, hs, cmb);
   return after_launch(what, st);
 }
 
 template <int MODE>
 moe_status launch_gemm(const uint8_t* aq, const float* as, const int* a_row, int64_t a_rows,
                        const uint8_t* bq, const float* bs, const int* offsets, int G, int64_t M, int N,
-                       int K, void* out, float* hs, hipStream_t st, const char* what) {
+                       int K, void* out, float* hs, hipStream_t st, const char* what,
+                       const CombineArgs& cmb = CombineArgs{}) {
   const int n_tiles = MODE == OUT_SWIGLU ? (N / 2) / 128 : (N + kBN - 1) / kBN;
   if (n_tiles > kMaxNTiles) return fail(MOE_ERR_UNSUPPORTED, "%s: N=%d too large", what, N);
-  return launch_cfg<MODE, CfgS>(aq, as, a_row, a_rows, bq, bs, offsets, G, M, N, K, n_tiles, out, hs, st, what);
+  return launch_cfg<MODE, CfgS>(aq, as, a_row, a_rows, bq, bs, offsets, G, M, N, K, n_tiles, out, hs, cmb, st,
+                                what);
 }
 
 moe_status check_gemm_args(const uint8_t* aq, const float* as, const int32_t* a_row, int64_t a_rows,
@@ -614,4 +735,46 @@ extern "C" moe_status grouped_gemm_fp8_swiglu(const uint8_t* aq, const float* as
   hipStream_t st = as_stream(stream);
   return launch_gemm<OUT_SWIGLU>(aq, as, a_row, a_rows, bq, bs, group_offsets, G, M, 2 * I, K, hq, hs, st,
                                  "grouped_gemm_fp8_swiglu");
+}
+
+extern "C" moe_status grouped_gemm_fp8_combine_workspace_size(int32_t T, int32_t N, size_t* bytes) {
+  clear_detail();
+  MOE_REQUIRE(bytes, MOE_ERR_NULL, "bytes is required");
+  MOE_REQUIRE(T >= 0 && N > 0, MOE_ERR_SHAPE, "T=%d N=%d", T, N);
+  *bytes = (size_t)T * (size_t)((N + kBN - 1) / kBN) * sizeof(int32_t);
+  return MOE_OK;
+}
+
+extern "C" moe_status grouped_gemm_fp8_combine(const uint8_t* aq, const float* as, const uint8_t* bq,
+                                               const float* bs, const int32_t* group_offsets, int32_t G, int64_t M,
+                                               int32_t N, int32_t K, float* c, const int32_t* src_token,
+                                               const int32_t* dst_row, const float* topk_gate, const float* shared,
+                                               int32_t T, int32_t topk, uint16_t* y_bf16, int32_t* counters,
+                                               size_t counters_bytes, void* stream) {
+  clear_detail();
+  MOE_REQUIRE(T >= 0 && topk >= 1, MOE_ERR_SHAPE, "T=%d topk=%d", T, topk);
+  MOE_REQUIRE(M == (int64_t)T * topk, MOE_ERR_SHAPE, "M=%lld must equal T*topk=%lld (no token dropped)",
+              (long long)M, (long long)T * topk);
+  moe_status stt = check_gemm_args(aq, as, nullptr, 0, bq, bs, group_offsets, G, M, N, K);
+  if (stt != MOE_OK || M == 0) return stt;
+  MOE_REQUIRE(c && src_token && dst_row && topk_gate && y_bf16 && counters, MOE_ERR_NULL,
+              "c, src_token, dst_row, topk_gate, y and counters are required");
+  MOE_REQUIRE(aligned(c, 16) && aligned(shared, 16) && aligned(y_bf16, 16) && aligned(src_token, 4) &&
+                  aligned(dst_row, 4) && aligned(topk_gate, 4) && aligned(counters, 4),
+              MOE_ERR_ALIGN, "c, shared and y need 16-byte alignment, index arrays 4-byte");
+  size_t need = 0;
+  grouped_gemm_fp8_combine_workspace_size(T, N, &need);
+  MOE_REQUIRE(counters_bytes >= need, MOE_ERR_WORKSPACE, "counters %zu < %zu bytes", counters_bytes, need);
+  CombineArgs cb;
+  cb.row_token = src_token;
+  cb.dst_row = dst_row;
+  cb.gate = topk_gate;
+  cb.shared = shared;
+  cb.y = y_bf16;
+  cb.counters = counters;
+  cb.T = T;
+  cb.topk = topk;
+  cb.M = M;
+  return launch_gemm<OUT_COMBINE>(aq, as, nullptr, 0, bq, bs, group_offsets, G, M, N, K, c, nullptr,
+                                  as_stream(stream), "grouped_gemm_fp8_combine", cb);
 }

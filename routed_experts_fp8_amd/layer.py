@@ -47,13 +47,24 @@ class MoEForward:
     whole forward on the current stream and returns y (bf16 [T, H])."""
 
     def __init__(self, T, H, E, I, route, weights, device, fused=True, shared_I=None, overlap_shared=True,
-                 router_weight=None):
+                 router_weight=None, fuse_route_permute=False, fuse_combine=False):
         self.T, self.H, self.E, self.I = T, H, E, I
         self.route = dict(route)
         self.K = route["K"] if route["mode"] == "sigmoid_bias" else route["n_groups"] * route["k_per_group"]
         self.w = weights
         self.fused = fused
         self.shared_I = shared_I
+        # Routing + the permutation's index maps in one launch
+        # (moe_route_permute) and the combine inside the down projection's
+        # epilogue (grouped_gemm_fp8_combine): bit-identical to the separate
+        # launches, and off by default because both measure slower on
+        # MI355X.  Workgroups that hand data to workgroups on other XCDs need
+        # a device-scope release (a write-back of the XCD's L2) per
+        # workgroup or tile, which costs more than the kernel boundaries it
+        # removes, and the combine's row gathers stall the GEMM tile
+        # pipeline, while the separate combine streams at about 5 TB/s.
+        self.fuse_route_permute = fuse_route_permute
+        self.fuse_combine = fuse_combine
         K, M = self.K, T * self.K
         dev = device
         e = lambda shape, dt: torch.empty(shape, dtype=dt, device=dev)
@@ -65,6 +76,10 @@ class MoEForward:
             hq=e((M, I), torch.uint8), hs=e((M, I // 128), torch.float32),
             c2=e((M, H), torch.float32), y=e((T, H), torch.bfloat16),
             ws=e((L.moe_permute_workspace_size(T, K, E),), torch.uint8),
+            # both keep counters between calls and must start zero-filled
+            rp_ws=torch.zeros((L.moe_route_permute_workspace_size(T, K, E),), dtype=torch.uint8, device=dev),
+            combine_ctr=torch.zeros((max(L.grouped_gemm_fp8_combine_workspace_size(T, H) // 4, 1),),
+                                    dtype=torch.int32, device=dev),
             one_group=torch.tensor([0, T], dtype=torch.int32, device=dev),
         )
         if not fused:
@@ -84,7 +99,7 @@ class MoEForward:
             if not fused:
                 self.buf["sc1"] = e((T, 2 * shared_I), torch.float32)
 
-    def _ffn(self, aq, as_, offsets, w13q, w13s, w2q, w2s, hq, hs, c2, c1, mark, a_row=None):
+    def _gemm1(self, aq, as_, offsets, w13q, w13s, hq, hs, c1, a_row=None):
         if self.fused:
             L.grouped_gemm_fp8_swiglu(aq, as_, w13q, w13s, offsets, hq=hq, hs=hs, a_row=a_row)
         else:
@@ -93,6 +108,9 @@ class MoEForward:
             else:
                 L.grouped_gemm_fp8_blockscaled_gather(aq, as_, a_row, w13q, w13s, offsets, c=c1)
             L.swiglu(c1, hq=hq, hs=hs)
+
+    def _ffn(self, aq, as_, offsets, w13q, w13s, w2q, w2s, hq, hs, c2, c1, mark, a_row=None):
+        self._gemm1(aq, as_, offsets, w13q, w13s, hq, hs, c1, a_row=a_row)
         mark("gemm1")
         L.grouped_gemm_fp8_blockscaled(hq, hs, w2q, w2s, offsets, c=c2)
         mark("gemm2")
@@ -142,22 +160,49 @@ class MoEForward:
                           out=dict(offsets=b["offsets"], dst_row=b["dst_row"], src_token=b["src_token"]))
             mark("permute")
 
+        def route_permute():
+            mode = r["mode"]
+            L.moe_route_permute(logits, bias if mode == "sigmoid_bias" else None, self.K, mode,
+                                n_groups=r.get("n_groups", 1), k_per_group=r.get("k_per_group"),
+                                normalize=r.get("normalize", True), workspace=b["rp_ws"],
+                                out=dict(topk_idx=b["idx"], topk_gate=b["gate"], offsets=b["offsets"],
+                                         dst_row=b["dst_row"], src_token=b["src_token"]))
+            mark("route_permute")
+
+        def join_shared():
+            nonlocal shared
+            if self.shared_I and self.side is None:
+                self._ffn(b["xq"], b["xs"], b["one_group"], w["sw13q"], w["sw13s"], w["sw2q"], w["sw2s"],
+                          b["shq"], b["shs"], b["sc2"], b.get("sc1"), lambda n: mark("shared_" + n))
+                shared = b["sc2"]
+            elif self.side is not None:
+                torch.cuda.current_stream().wait_stream(self.side)
+                mark("shared_join")
+
         # The shared expert needs only x's codes: it is forked first, and the
         # routing, permutation and routed GEMM1 fill the CUs its last partial
         # wave of workgroups leaves idle.
         quant()
         fork()
-        route()
-        permute()
-        self._ffn(b["xq"], b["xs"], b["offsets"], w["w13q"], w["w13s"], w["w2q"], w["w2s"],
-                  b["hq"], b["hs"], b["c2"], b.get("c1"), mark, a_row=b["src_token"])
-        if self.shared_I and self.side is None:
-            self._ffn(b["xq"], b["xs"], b["one_group"], w["sw13q"], w["sw13s"], w["sw2q"], w["sw2s"],
-                      b["shq"], b["shs"], b["sc2"], b.get("sc1"), lambda n: mark("shared_" + n))
-            shared = b["sc2"]
-        elif self.side is not None:
-            torch.cuda.current_stream().wait_stream(self.side)
-            mark("shared_join")
+        if self.fuse_route_permute:
+            route_permute()
+        else:
+            route()
+            permute()
+        self._gemm1(b["xq"], b["xs"], b["offsets"], w["w13q"], w["w13s"], b["hq"], b["hs"], b.get("c1"),
+                    a_row=b["src_token"])
+        mark("gemm1")
+        if self.fuse_combine:
+            # the epilogue reads the shared expert's output: join first
+            join_shared()
+            L.grouped_gemm_fp8_combine(b["hq"], b["hs"], w["w2q"], w["w2s"], b["offsets"], b["src_token"],
+                                       b["dst_row"], b["gate"], shared, c=b["c2"], y=b["y"],
+                                       counters=b["combine_ctr"])
+            mark("gemm2_combine")
+            return b["y"]
+        L.grouped_gemm_fp8_blockscaled(b["hq"], b["hs"], w["w2q"], w["w2s"], b["offsets"], c=b["c2"])
+        mark("gemm2")
+        join_shared()
         L.moe_combine(b["c2"], b["dst_row"], b["gate"], shared, out=b["y"])
         mark("combine")
         return b["y"]

@@ -302,3 +302,45 @@ def test_permute_noalloc_errors():
     assert f(P, 8, 2, 8, N0, N0, 0, N0, P, P, N0, N0, S) == NULL                # no offsets
     assert f(P, 600000, 2, 256, N0, N0, 0, P, P, P, N0, N0, S) == WS            # beyond the 4 MiB scratch
     assert "scratch" in _detail()
+
+
+def test_route_permute_errors():
+    """The single-launch routing + permutation checks moe_route's and
+    moe_permute's arguments and its workspace on the host (every call here
+    fails validation; T = 0 would still launch, to write the zero offsets)."""
+    n = ctypes.c_size_t(0)
+    assert L.lib.moe_route_permute_workspace_size(4096, 8, 256, ctypes.byref(n)) == OK
+    assert n.value == 256 + 2 * 64 * 256 * 4          # header + counts and base rows of 64-token blocks
+    assert L.lib.moe_route_permute_workspace_size(0, 8, 256, ctypes.byref(n)) == OK and n.value == 256
+    assert L.lib.moe_route_permute_workspace_size(10, 9, 8, ctypes.byref(n)) == SHAPE
+    f = L.lib.moe_route_permute
+    sig, grp = L.ROUTE_SIGMOID_BIAS, L.ROUTE_SOFTMAX_GROUPED
+    big = 1 << 20
+    assert f(P, N0, 4, 2048, 8, 1, 8, sig, 1, P, P, P, P, P, P, big, S) == UNSUP      # E > 1024
+    assert f(P, N0, 4, 16, 17, 1, 17, sig, 1, P, P, P, P, P, P, big, S) == SHAPE      # K > E
+    assert f(P, N0, 4, 18, 4, 4, 1, grp, 0, P, P, P, P, P, P, big, S) == SHAPE        # E % G
+    assert f(P, N0, 4, 16, 4, 4, 1, grp, 1, P, P, P, P, P, P, big, S) == UNSUP        # no renormalisation
+    assert f(P, N0, 4, 16, 4, 1, 4, 9, 1, P, P, P, P, P, P, big, S) == UNSUP          # mode
+    assert f(N0, N0, 4, 16, 4, 1, 4, sig, 1, P, P, P, P, P, P, big, S) == NULL        # logits
+    assert f(P, N0, 4, 16, 4, 1, 4, sig, 1, P, P, N0, P, P, P, big, S) == NULL        # offsets
+    assert f(P, N0, 4, 16, 4, 1, 4, sig, 1, P, P, P, P, P, N0, big, S) == NULL        # workspace
+    assert f(P, N0, 4, 16, 4, 1, 4, sig, 1, P, P, P, P, P, PM, big, S) == ALIGN       # workspace 16 B
+    assert f(P, N0, 4, 16, 4, 1, 4, sig, 1, P, P, P, P, P, P, 255, S) == WS
+    assert f(P, N0, 1 << 28, 16, 16, 1, 16, sig, 1, P, P, P, P, P, P, big, S) == UNSUP  # T*K
+
+
+def test_gemm_combine_errors():
+    n = ctypes.c_size_t(0)
+    assert L.lib.grouped_gemm_fp8_combine_workspace_size(4096, 7168, ctypes.byref(n)) == OK
+    assert n.value == 4096 * 28 * 4
+    assert L.lib.grouped_gemm_fp8_combine_workspace_size(4, 384, ctypes.byref(n)) == OK and n.value == 4 * 2 * 4
+    f = L.lib.grouped_gemm_fp8_combine
+    ws = 1 << 20
+    assert f(P, P, P, P, P, 4, 64, 256, 128, P, P, P, P, N0, 16, 3, P, P, ws, S) == SHAPE    # M != T*topk
+    assert f(P, P, P, P, P, 4, 64, 100, 128, P, P, P, P, N0, 16, 4, P, P, ws, S) == SHAPE    # N % 128
+    assert f(P, P, P, P, P, 4, 64, 256, 128, P, N0, P, P, N0, 16, 4, P, P, ws, S) == NULL    # src_token
+    assert f(P, P, P, P, P, 4, 64, 256, 128, P, P, P, P, N0, 16, 4, P, N0, ws, S) == NULL    # counters
+    assert f(P, P, P, P, P, 4, 64, 256, 128, P, P, P, P, PM, 16, 4, P, P, ws, S) == ALIGN    # shared
+    assert f(P, P, P, P, P, 4, 64, 256, 128, P, P, P, P, N0, 16, 4, P, P, 63, S) == WS       # 16*1*4 bytes
+    assert f(P, P, P, P, P, 4, 64, 256, 128, P, P, P, P, N0, 16, 0, P, P, ws, S) == SHAPE    # topk
+    assert f(N0, N0, N0, N0, P, 4, 0, 256, 128, N0, N0, N0, N0, N0, 0, 4, N0, N0, 0, S) == OK  # empty

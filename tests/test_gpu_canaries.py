@@ -113,6 +113,32 @@ def test_route_permute_combine_bands():
                      lambda o: R.moe_combine(y_perm, dst, gate, sh, out=o["y"]))
 
 
+def test_fused_stage_bands():
+    """moe_route_permute writes every element of its five outputs; the down
+    projection with the fused combine writes every element of c and y."""
+    T, E, K = 333, 40, 6
+    logits = to_dev(RNG.standard_normal((T, E)).astype(F32))
+    bias = to_dev((RNG.standard_normal(E) * 0.01).astype(F32))
+    ws = torch.zeros(R.moe_route_permute_workspace_size(T, K, E), dtype=torch.uint8, device=dev())
+    outs = {"topk_idx": ((T, K), torch.int32), "topk_gate": ((T, K), torch.float32),
+            "offsets": ((E + 1,), torch.int32), "dst_row": ((T, K), torch.int32),
+            "src_token": ((T * K,), torch.int32)}
+    o = _all_written(outs, lambda o: R.moe_route_permute(logits, bias, K, workspace=ws, out=o))
+    idx = to_dev(o["topk_idx"].view(np.int32).reshape(T, K))
+    perm = R.moe_permute(idx, E)
+    N, Kd = 384, 256                                    # a half n-tile
+    aq, as_ = O.quant_act_1x128(RNG.standard_normal((T * K, Kd)).astype(F32))
+    bq, bs = O.quant_weight_128x128((RNG.standard_normal((E, N, Kd)) * 0.02).astype(F32))
+    gate = to_dev(RNG.uniform(0, 1, (T, K)).astype(F32))
+    shared = to_dev(RNG.standard_normal((T, N)).astype(F32))
+    ctr = torch.zeros(R.grouped_gemm_fp8_combine_workspace_size(T, N) // 4, dtype=torch.int32, device=dev())
+    _all_written({"c": ((T * K, N), torch.float32), "y": ((T, N), torch.bfloat16)},
+                 lambda o: R.grouped_gemm_fp8_combine(to_dev(aq), to_dev(as_), to_dev(bq), to_dev(bs),
+                                                      perm["offsets"], perm["src_token"], perm["dst_row"], gate,
+                                                      shared, c=o["c"], y=o["y"], counters=ctr))
+    assert not ctr.any()
+
+
 def test_quantiser_and_transpose_bands():
     x = to_dev(RNG.standard_normal((77, 640)).astype(F32))
     _all_written({"q": ((77, 640), torch.uint8), "s": ((77, 5), torch.float32)},

@@ -216,3 +216,33 @@ def test_fullsize_layer_forward_end_to_end(key):
           f"{code_diff / n_rows:.2e}; gemm2 worst {worst2:.3g}; y within 1 bf16 ulp: timed forward "
           f"{within:.4f}, fed the oracle's h {within_m:.6f} (max {int(ulp_m.max())} ulp)")
     assert within_m >= 0.99, within_m
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("key", ["dsv3", "moge", "skewed", "skewed_dead"])
+def test_fullsize_stage_fusions_bit_identical(key):
+    """At the full workload sizes, routing + permutation in one launch and
+    the combine in the down projection's epilogue write the same bits as
+    the separate launches into every buffer of the forward (routing,
+    permutation, h, the expert outputs and y), over repeated calls, and
+    leave their counters zero."""
+    cfg, d = _inputs(key)
+    T, H, E, I = cfg["T"], cfg["H"], cfg["E"], cfg["I"]
+    w = R.quantize_weights(d["w13"], d["w2"], d.get("sw13"), d.get("sw2"))
+    del d["w13"], d["w2"]
+    keys = ("idx", "gate", "offsets", "dst_row", "src_token", "hq", "hs", "c2", "y")
+    ref = None
+    for fused_stages in (False, True):
+        fwd = R.MoEForward(T, H, E, I, cfg["route"], w, dev(), fused=True, shared_I=cfg.get("shared_I"),
+                           fuse_route_permute=fused_stages, fuse_combine=fused_stages)
+        for _ in range(2):
+            fwd(d["x"], d["logits"], d["bias"])
+        torch.cuda.synchronize()
+        got = {k: fwd.buf[k].view(torch.uint8).clone() for k in keys}
+        assert not fwd.buf["combine_ctr"].any() and not fwd.buf["rp_ws"][:256].any()
+        if ref is None:
+            ref = got
+        else:
+            for k in keys:
+                assert torch.equal(got[k], ref[k]), k
+        del fwd

@@ -42,11 +42,11 @@ def _variant(name):
     return cfg
 
 
-def run_layer(cfg, fused, seed=0, overlap_shared=True):
+def run_layer(cfg, fused, seed=0, overlap_shared=True, **fusions):
     d = synth.layer_inputs(cfg, dev(), seed=seed)
     w = R.quantize_weights(d["w13"], d["w2"], d.get("sw13"), d.get("sw2"))
     fwd = R.MoEForward(cfg["T"], cfg["H"], cfg["E"], cfg["I"], cfg["route"], w, dev(), fused=fused,
-                       shared_I=cfg.get("shared_I"), overlap_shared=overlap_shared)
+                       shared_I=cfg.get("shared_I"), overlap_shared=overlap_shared, **fusions)
     y = fwd(d["x"], d["logits"], d["bias"])
     torch.cuda.synchronize()
     return d, w, fwd, y
@@ -154,6 +154,40 @@ def test_layer_matches_oracle(name, fused):
     print(name, fused, stats)
 
 
+@pytest.mark.parametrize("name", ["tiny_sigmoid_shared", "small_moge"])
+def test_layer_fused_combine_matches_oracle(name):
+    """The forward with the combine inside the down projection's epilogue
+    meets the same oracle rule."""
+    cfg = _variant(name)
+    d, w, fwd, y = run_layer(cfg, True, fuse_combine=True)
+    print(name, check_layer_against_oracle(cfg, d, w, fwd, y))
+
+
+@pytest.mark.parametrize("name", ["tiny_sigmoid_shared", "small_moge"])
+def test_layer_stage_fusions_are_bit_identical(name):
+    """Routing + permutation in one launch and the combine in the down
+    projection's epilogue change no bit of any buffer the forward writes,
+    with the shared expert on its side stream or in line, over repeated
+    calls."""
+    cfg = _variant(name)
+    keys = ("idx", "gate", "offsets", "dst_row", "src_token", "hq", "hs", "c2", "y")
+    ref = None
+    for frp in (False, True):
+        for fc in (False, True):
+            for overlap in (True, False):
+                d, _, fwd, _ = run_layer(cfg, True, overlap_shared=overlap, fuse_route_permute=frp,
+                                         fuse_combine=fc)
+                for _ in range(2):
+                    fwd(d["x"], d["logits"], d["bias"])
+                torch.cuda.synchronize()
+                got = {k: np_(fwd.buf[k].view(torch.uint8)) for k in keys}
+                if ref is None:
+                    ref = got
+                for k in keys:
+                    assert np.array_equal(got[k], ref[k]), (k, frp, fc, overlap)
+                assert not fwd.buf["combine_ctr"].any() and not fwd.buf["rp_ws"][:256].any()
+
+
 def test_layer_fused_equals_unfused_and_is_deterministic():
     cfg = _variant("tiny_sigmoid_shared")
     _, _, _, y1 = run_layer(cfg, True)
@@ -177,13 +211,16 @@ def test_layer_shared_expert_side_stream_equals_in_line():
     assert np.array_equal(bf16_bits(y), bf16_bits(y2))
 
 
-def test_layer_forward_in_a_hip_graph():
+@pytest.mark.parametrize("fuse_combine", [False, True])
+def test_layer_forward_in_a_hip_graph(fuse_combine):
     """The forward allocates nothing and joins its side stream, so it can be
     captured once in a HIP graph and replayed: every replay (with the
     program's own eager work and synchronisations in between) gives the
-    eager result bit for bit, also after the inputs change in place."""
+    eager result bit for bit, also after the inputs change in place.  The
+    fused stages' counters live in the layer's workspaces and are reset by
+    the kernels themselves, so replays need no clearing either."""
     cfg = _variant("tiny_sigmoid_shared")
-    d, w, fwd, y_eager = run_layer(cfg, True)
+    d, w, fwd, y_eager = run_layer(cfg, True, fuse_combine=fuse_combine, fuse_route_permute=fuse_combine)
     ref = bf16_bits(y_eager)
     x, logits, bias = d["x"].clone(), d["logits"].clone(), d["bias"].clone()
     s = torch.cuda.Stream()
