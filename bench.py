@@ -52,12 +52,14 @@ def parse():
     p.add_argument("--config", default="dsv3")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true")
-    p.add_argument("--section", choices=["layer", "backward", "train"], default="layer",
+    p.add_argument("--section", choices=["layer", "backward", "train", "wgrad"], default="layer",
                    help="layer: the forward bench line (default); backward: time only the input-side "
                         "backward + weight gradients of the same workload, K steps after W warm-ups "
                         "(for per-kernel profiles); train: a whole training step of the layer (weight "
                         "quantisation and transpose, forward, backward, weight gradients, bias update); "
-                        "the last two print their own JSON line")
+                        "wgrad: only the routed weight-gradient GEMMs (down and gate|up, float32 and "
+                        "bf16 output) on operands prepared once, for per-kernel profiles and counters; "
+                        "the last three print their own JSON line")
     return p.parse_args()
 
 
@@ -536,6 +538,47 @@ def backward_section(args, cfg, d, w, torch, R, synth):
     print(json.dumps(line), flush=True)
 
 
+def wgrad_section(args, cfg, d, w, torch, R, synth):
+    """K timed steps of the routed weight-gradient GEMMs alone: dW2 and dW13
+    with float32 and with bf16 output, on the 128x1-quantised operands of one
+    backward pass (prepared once, untimed); one JSON line with each launch's
+    time and algorithmic bytes."""
+    T, H, E, I = cfg["T"], cfg["H"], cfg["E"], cfg["I"]
+    dev = d["x"].device
+    wt = R.transpose_weights(w)
+    fwd = R.MoEForward(T, H, E, I, cfg["route"], w, dev, fused=False, shared_I=cfg.get("shared_I"))
+    fwd(d["x"], d["logits"], d["bias"])
+    dy = synth.output_grad(T, H, dev, seed=4)
+    bwd = R.MoEBackward(fwd, wt, weight_grad=True)
+    bwd(dy, d["logits"])
+    wg = R.MoEWeightGrad(bwd)
+    wg(d["x"], dy)
+    del wt
+    wb = wg.buf
+    b2, b13 = wgrad_bytes(E, H, I, wg)
+    launches = {}
+    for name, (a, sa, b, sb), shape, nbytes in (
+            ("down", (wb["dc2t"], wb["dc2ts"], wb["ht"], wb["hts"]), (E, H, I), b2),
+            ("gate_up", (wb["d1t"], wb["d1ts"], wb["xt"], wb["xts"]), (E, 2 * I, H), b13)):
+        for dt, tag in ((torch.float32, "f32"), (torch.bfloat16, "bf16")):
+            c = torch.empty(shape, dtype=dt, device=dev)
+            out_bytes = shape[0] * shape[1] * shape[2] * (4 if dt == torch.float32 else 2)
+            launches[f"{name}_wgrad_{tag}"] = (lambda a=a, sa=sa, b=b, sb=sb, c=c: R.grouped_wgrad_fp8(
+                a, sa, b, sb, wb["poff"], c=c), nbytes - 4 * shape[0] * shape[1] * shape[2] + out_bytes)
+    for _ in range(args.warmup):
+        for fn, _ in launches.values():
+            fn()
+    torch.cuda.synchronize()
+    rows = {}
+    for k, (fn, nbytes) in launches.items():
+        ms = time_op(fn, args.steps, torch)
+        rows[k] = dict(ms=ms, bytes=nbytes, GBps=nbytes / ms / 1e6, frac_hbm=nbytes / ms / 1e6 / HBM_PEAK_GBS)
+    line = {"metric": "routed FP8 weight-gradient GEMMs, GB/s (algorithmic bytes), 1 GPU", "unit": "GB/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "dtype": "fp8_e4m3", "data": "synthetic",
+            "config": {"workload": cfg["name"], "padded_rows": wg.ld}, "launches": rows}
+    print(json.dumps(line), flush=True)
+
+
 def cpu_baseline_train(cfg, d, dy, n_experts=2):
     """The oracle's training step on a bounded sample, scaled to the layer:
     routing, activation quantisation and permutation of all tokens; for
@@ -678,6 +721,9 @@ def main():
     w = R.quantize_weights(d["w13"], d["w2"], d.get("sw13"), d.get("sw2"))
     if args.section == "backward":
         backward_section(args, cfg, d, w, torch, R, synth)
+        return
+    if args.section == "wgrad":
+        wgrad_section(args, cfg, d, w, torch, R, synth)
         return
     if args.section == "train":
         del w
