@@ -46,6 +46,8 @@
  *  - Pointers to 16-byte vectors (codes, bf16 rows, fp32 rows) must be
  *    16-byte aligned (MOE_ERR_ALIGN otherwise); index and scale arrays need
  *    4-byte alignment.
+ *  - Operands of more than 2^40 elements (beyond any device memory) are
+ *    refused with MOE_ERR_UNSUPPORTED, before any size arithmetic.
  */
 #ifndef MOEFP8_H
 #define MOEFP8_H
@@ -71,12 +73,18 @@ enum {
   MOE_ERR_HIP = 6          /* the HIP runtime reported an error             */
 };
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+/* Element type and routing mode selectors are plain 32-bit integers (with
+ * named values) rather than C enum types, so any value a caller passes is
+ * well defined on the library side and an unknown one is refused with
+ * MOE_ERR_UNSUPPORTED. */
+typedef int32_t moe_dtype;
+enum { MOE_F32 = 0, MOE_BF16 = 1 };
 
-typedef enum {
+typedef int32_t moe_route_mode;
+enum {
   MOE_ROUTE_SIGMOID_BIAS = 0,   /* [DSV3-MOE]   */
   MOE_ROUTE_SOFTMAX_GROUPED = 1 /* [PANGU-MOGE] */
-} moe_route_mode;
+};
 
 /* Text of a status code (static storage). */
 MOE_API const char* moe_status_string(moe_status s);
@@ -121,7 +129,7 @@ MOE_API moe_status moe_route(const float* logits, const float* bias, int32_t T, 
  *  Every finite or infinite input is defined; NaN inputs give unspecified
  *  values.
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE (n < 0), MOE_ERR_ALIGN (x, y 16-byte),
- *         MOE_ERR_UNSUPPORTED (n >= 2^41).
+ *         MOE_ERR_UNSUPPORTED (n above 2^40).
  */
 MOE_API moe_status moe_sigmoid_f32(const float* x, int64_t n, float* y, void* stream);
 

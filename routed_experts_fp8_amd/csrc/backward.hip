@@ -238,6 +238,8 @@ extern "C" moe_status moe_combine_backward(const uint16_t* dy_bf16, const float*
   MOE_REQUIRE(T >= 0 && K >= 1 && H > 0 && H % 128 == 0, MOE_ERR_SHAPE,
               "T=%d K=%d H=%d (H a positive multiple of 128)", T, K, H);
   MOE_REQUIRE(K <= kMaxK, MOE_ERR_UNSUPPORTED, "K=%d > %d", K, kMaxK);
+  MOE_REQUIRE(elems_ok((int64_t)T * K, H), MOE_ERR_UNSUPPORTED, "T*K=%lld x H=%d above 2^40 elements",
+              (long long)T * K, H);
   if (T == 0) return MOE_OK;
   MOE_REQUIRE(dy_bf16 && y_perm && dst_row && topk_gate && dq && ds && d_gate, MOE_ERR_NULL,
               "every array is required");
@@ -255,6 +257,8 @@ extern "C" moe_status swiglu_backward(const float* gate_up, const float* dh, int
   clear_detail();
   MOE_REQUIRE(M >= 0 && I > 0 && I % 128 == 0, MOE_ERR_SHAPE, "M=%lld I=%d (I a positive multiple of 128)",
               (long long)M, I);
+  MOE_REQUIRE(elems_ok(M, 2 * (int64_t)I), MOE_ERR_UNSUPPORTED, "M=%lld x 2I=%lld above 2^40 elements",
+              (long long)M, 2 * (long long)I);
   if (M == 0) return MOE_OK;
   MOE_REQUIRE(gate_up && dh && dq && ds, MOE_ERR_NULL, "gate_up, dh, dq and ds are required");
   MOE_REQUIRE(aligned(gate_up, 16) && aligned(dh, 16) && aligned(dq, 4) && aligned(ds, 4) && aligned(d, 16),
@@ -279,7 +283,7 @@ extern "C" moe_status moe_route_backward(const float* logits, const int32_t* top
   MOE_REQUIRE(aligned(logits, 4) && aligned(topk_idx, 4) && aligned(d_gate, 4) && aligned(d_logits, 4),
               MOE_ERR_ALIGN, "4-byte alignment required");
   hipStream_t st = as_stream(stream);
-  route_backward_kernel<<<(unsigned)((T + 3) / 4), 256, 0, st>>>(
+  route_backward_kernel<<<(unsigned)(((int64_t)T + 3) / 4), 256, 0, st>>>(
       logits, topk_idx, d_gate, T, E, K, mode == MOE_ROUTE_SOFTMAX_GROUPED ? 1 : 0, normalize_topk, d_logits);
   return after_launch("moe_route_backward", st);
 }

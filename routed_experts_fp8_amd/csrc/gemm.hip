@@ -645,7 +645,7 @@ moe_status launch_gemm(const uint8_t* aq, const float* as, const int* a_row, int
                        const uint8_t* bq, const float* bs, const int* offsets, int G, int64_t M, int N,
                        int K, void* out, float* hs, hipStream_t st, const char* what,
                        const CombineArgs& cmb = CombineArgs{}) {
-  const int n_tiles = MODE == OUT_SWIGLU ? (N / 2) / 128 : (N + kBN - 1) / kBN;
+  const int n_tiles = (int)(MODE == OUT_SWIGLU ? (N / 2) / 128 : ((int64_t)N + kBN - 1) / kBN);
   if (n_tiles > kMaxNTiles) return fail(MOE_ERR_UNSUPPORTED, "%s: N=%d too large", what, N);
   return launch_cfg<MODE, CfgS>(aq, as, a_row, a_rows, bq, bs, offsets, G, M, N, K, n_tiles, out, hs, cmb, st,
                                 what);
@@ -728,6 +728,7 @@ extern "C" moe_status grouped_gemm_fp8_swiglu(const uint8_t* aq, const float* as
                                               void* stream) {
   clear_detail();
   MOE_REQUIRE(I > 0 && I % 128 == 0, MOE_ERR_SHAPE, "I=%d must be a positive multiple of 128", I);
+  MOE_REQUIRE(I <= 128 * kMaxNTiles, MOE_ERR_UNSUPPORTED, "I=%d > %d", I, 128 * kMaxNTiles);
   moe_status stt = check_gemm_args(aq, as, a_row, a_rows, bq, bs, group_offsets, G, M, 2 * I, K);
   if (stt != MOE_OK || M == 0) return stt;
   MOE_REQUIRE(hq && hs, MOE_ERR_NULL, "hq and hs are required");
@@ -741,7 +742,7 @@ extern "C" moe_status grouped_gemm_fp8_combine_workspace_size(int32_t T, int32_t
   clear_detail();
   MOE_REQUIRE(bytes, MOE_ERR_NULL, "bytes is required");
   MOE_REQUIRE(T >= 0 && N > 0, MOE_ERR_SHAPE, "T=%d N=%d", T, N);
-  *bytes = (size_t)T * (size_t)((N + kBN - 1) / kBN) * sizeof(int32_t);
+  *bytes = (size_t)T * (((size_t)N + kBN - 1) / kBN) * sizeof(int32_t);
   return MOE_OK;
 }
 

@@ -25,6 +25,12 @@ inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s);
 
 inline unsigned ceil_div_u(int64_t a, int64_t b) { return (unsigned)((a + b - 1) / b); }
 
+// Element counts above 2^40 exceed any device memory; entry points refuse
+// them (MOE_ERR_UNSUPPORTED) before any size arithmetic that could overflow.
+constexpr int64_t kMaxElems = int64_t(1) << 40;
+// a * b <= kMaxElems for non-negative a, b (no overflow in the test itself).
+inline bool elems_ok(int64_t a, int64_t b) { return a >= 0 && b >= 0 && (b == 0 || a <= kMaxElems / b); }
+
 }  // namespace moefp8
 
 #define MOE_REQUIRE(cond, status, ...)                  \

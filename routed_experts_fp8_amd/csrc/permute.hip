@@ -6,7 +6,9 @@
 //   1. count   : per block of 256 tokens, an LDS histogram of expert ids
 //                (integer atomics: the counts do not depend on order);
 //   2. scan    : one workgroup turns the [blocks, E] counts into expert
-//                offsets and per-(block, expert) base rows;
+//                offsets and per-(block, expert) base rows (each expert's
+//                blocks split over 1024 / E' threads, E' = E rounded up to a
+//                power of two);
 //   3. rank    : per token block, an LDS bit matrix [E][256] marks which
 //                tokens picked each expert; the rank of token t inside
 //                expert e is the popcount of e's bits below t, so rows follow
@@ -36,35 +38,75 @@ __global__ __launch_bounds__(kBT) void permute_count_kernel(const int* __restric
   for (int e = threadIdx.x; e < E; e += kBT) counts[(int64_t)blockIdx.x * E + e] = hist[e];
 }
 
-// One workgroup of 1024 threads; thread e owns expert e.
+// One workgroup of 1024 threads.  Experts are padded to Ep (a power of two)
+// and each gets P = 1024 / Ep threads, thread (e, part) summing a run of
+// consecutive blocks, so the count rows stream in with P-fold parallelism.
 __global__ __launch_bounds__(1024) void permute_scan_kernel(const int* __restrict__ counts,
-                                                            int nblk, int E,
+                                                            int nblk, int E, int Ep,
                                                             int* __restrict__ base,
                                                             int* __restrict__ offsets) {
-  __shared__ int sums[1024];
-  const int e = threadIdx.x;
-  int running = 0;
-  if (e < E)
-    for (int b = 0; b < nblk; ++b) {
-      const int c = counts[(int64_t)b * E + e];
-      base[(int64_t)b * E + e] = running;  // exclusive within expert e
-      running += c;
-    }
-  sums[e] = e < E ? running : 0;
-  __syncthreads();
-  // inclusive Hillis-Steele scan over experts
-  for (int d = 1; d < 1024; d <<= 1) {
-    const int v = e >= d ? sums[e - d] : 0;
-    __syncthreads();
-    sums[e] += v;
-    __syncthreads();
-  }
-  const int excl = sums[e] - (e < E ? running : 0);
+  __shared__ int sSeg[1024];  // [part][Ep]: a run's sum, then its exclusive prefix
+  __shared__ int sScan[1024];
+  const int tid = threadIdx.x;
+  const int P = 1024 / Ep, e = tid % Ep, part = tid / Ep;
+  const int S = (nblk + P - 1) / P;
+  const int b0 = min(part * S, nblk), b1 = min(b0 + S, nblk);
+  int seg = 0;
   if (e < E) {
-    offsets[e] = excl;
-    for (int b = 0; b < nblk; ++b) base[(int64_t)b * E + e] += excl;
+    int b = b0;
+    for (; b + 8 <= b1; b += 8) {
+      int v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = counts[(int64_t)(b + j) * E + e];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) seg += v[j];
+    }
+    for (; b < b1; ++b) seg += counts[(int64_t)b * E + e];
   }
-  if (e == E - 1) offsets[E] = sums[e];
+  sSeg[tid] = seg;
+  __syncthreads();
+  // per expert: exclusive prefix over its runs, and its total
+  int tot = 0;
+  if (tid < Ep) {
+    for (int p = 0; p < P; ++p) {
+      const int v = sSeg[p * Ep + tid];
+      sSeg[p * Ep + tid] = tot;
+      tot += v;
+    }
+  }
+  // inclusive Hillis-Steele scan of the totals over the Ep experts
+  sScan[tid] = tid < Ep ? tot : 0;
+  __syncthreads();
+  for (int d = 1; d < Ep; d <<= 1) {
+    const int v = (tid < Ep && tid >= d) ? sScan[tid - d] : 0;
+    __syncthreads();
+    if (tid < Ep) sScan[tid] += v;
+    __syncthreads();
+  }
+  const int total = sScan[Ep - 1];
+  __syncthreads();                  // every thread has read the total
+  if (tid < Ep) sScan[tid] -= tot;  // exclusive: expert tid's first row
+  __syncthreads();
+  if (tid < E) offsets[tid] = sScan[tid];
+  if (tid == 0) offsets[E] = total;
+  if (e < E) {
+    int run = sScan[e] + sSeg[part * Ep + e];
+    int b = b0;
+    for (; b + 8 <= b1; b += 8) {
+      int v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = counts[(int64_t)(b + j) * E + e];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        base[(int64_t)(b + j) * E + e] = run;
+        run += v[j];
+      }
+    }
+    for (; b < b1; ++b) {
+      base[(int64_t)b * E + e] = run;
+      run += counts[(int64_t)b * E + e];
+    }
+  }
 }
 
 __global__ __launch_bounds__(kBT) void permute_rank_kernel(const int* __restrict__ idx, int T,
@@ -125,7 +167,7 @@ extern "C" moe_status moe_permute_workspace_size(int32_t T, int32_t K, int32_t E
   MOE_REQUIRE(bytes, MOE_ERR_NULL, "bytes is required");
   MOE_REQUIRE(T >= 0 && K >= 1 && E >= 1 && K <= E, MOE_ERR_SHAPE, "T=%d K=%d E=%d", T, K, E);
   MOE_REQUIRE(E <= 1024, MOE_ERR_UNSUPPORTED, "E=%d > 1024", E);
-  const size_t nblk = (size_t)(T + kBT - 1) / kBT;
+  const size_t nblk = ((size_t)T + kBT - 1) / kBT;
   *bytes = 2 * nblk * (size_t)E * sizeof(int32_t) + 256;
   return MOE_OK;
 }
@@ -162,12 +204,14 @@ moe_status launch_permute(const int32_t* topk_idx, int32_t T, int32_t K, int32_t
                           const float* xs, int32_t H, int32_t* expert_offsets, int32_t* dst_row,
                           int32_t* src_token, uint8_t* aq, float* as, bool gather, void* workspace,
                           hipStream_t st, const char* what) {
-  const int nblk = (T + kBT - 1) / kBT;
+  const int nblk = (int)(((int64_t)T + kBT - 1) / kBT);
   int* counts = reinterpret_cast<int*>(workspace);
   int* base = counts + (size_t)nblk * E;
   if (nblk > 0)
     permute_count_kernel<<<nblk, kBT, E * sizeof(int), st>>>(topk_idx, T, K, E, counts);
-  permute_scan_kernel<<<1, 1024, 0, st>>>(counts, nblk, E, base, expert_offsets);
+  int Ep = 1;
+  while (Ep < E) Ep <<= 1;
+  permute_scan_kernel<<<1, 1024, 0, st>>>(counts, nblk, E, Ep, base, expert_offsets);
   if (nblk > 0)
     permute_rank_kernel<<<nblk, kBT, E * (kBT / 32) * sizeof(uint32_t), st>>>(topk_idx, T, K, E, base,
                                                                               dst_row, src_token);

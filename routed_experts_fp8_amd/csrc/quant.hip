@@ -172,6 +172,8 @@ extern "C" moe_status quant_act_1x128_e4m3(const void* x, moe_dtype x_dtype, int
   MOE_REQUIRE(x_dtype == MOE_F32 || x_dtype == MOE_BF16, MOE_ERR_UNSUPPORTED, "x_dtype %d", (int)x_dtype);
   MOE_REQUIRE(rows >= 0 && cols > 0 && cols % 128 == 0, MOE_ERR_SHAPE,
               "rows=%lld cols=%d (cols must be a positive multiple of 128)", (long long)rows, cols);
+  MOE_REQUIRE(elems_ok(rows, cols), MOE_ERR_UNSUPPORTED, "rows=%lld x cols=%d above 2^40 elements",
+              (long long)rows, cols);
   if (rows == 0) return MOE_OK;
   MOE_REQUIRE(x && q && scale, MOE_ERR_NULL, "x, q and scale are required");
   MOE_REQUIRE(aligned(x, 16) && aligned(q, 16) && aligned(scale, 4), MOE_ERR_ALIGN,
@@ -197,6 +199,8 @@ moe_status quant_weight_impl(const void* w, moe_dtype w_dtype, int32_t G, int32_
   MOE_REQUIRE(w_dtype == MOE_F32 || w_dtype == MOE_BF16, MOE_ERR_UNSUPPORTED, "w_dtype %d", (int)w_dtype);
   MOE_REQUIRE(G >= 0 && rows > 0 && cols > 0 && rows % 128 == 0 && cols % 128 == 0, MOE_ERR_SHAPE,
               "G=%d rows=%d cols=%d (rows, cols positive multiples of 128)", G, rows, cols);
+  MOE_REQUIRE(elems_ok((int64_t)G * rows, cols), MOE_ERR_UNSUPPORTED, "G=%d x %d x %d above 2^40 elements", G,
+              rows, cols);
   if (G == 0) return MOE_OK;
   MOE_REQUIRE(w && q && scale, MOE_ERR_NULL, "w, q and scale are required");
   MOE_REQUIRE(aligned(w, 16) && aligned(q, 16) && aligned(scale, 4) && aligned(qt, 16) && aligned(scale_t, 4),

@@ -99,8 +99,8 @@ extern "C" moe_status moe_sigmoid_f32(const float* x, int64_t n, float* y, void*
   if (n == 0) return MOE_OK;
   MOE_REQUIRE(x && y, MOE_ERR_NULL, "x and y are required");
   MOE_REQUIRE(aligned(x, 16) && aligned(y, 16), MOE_ERR_ALIGN, "x and y need 16-byte alignment");
+  MOE_REQUIRE(n <= kMaxElems, MOE_ERR_UNSUPPORTED, "n=%lld above 2^40", (long long)n);
   const int64_t blocks = (n + 1023) / 1024;
-  MOE_REQUIRE(blocks < (1LL << 31), MOE_ERR_UNSUPPORTED, "n=%lld too large", (long long)n);
   hipStream_t st = as_stream(stream);
   sigmoid_kernel<<<(unsigned)blocks, 256, 0, st>>>(x, n, y);
   return after_launch("moe_sigmoid_f32", st);

@@ -349,11 +349,11 @@ extern "C" moe_status moe_route_permute(const float* logits, const float* bias, 
   a.dst_row = dst_row;
   a.src_token = src_token;
   a.state = reinterpret_cast<RPState*>(workspace);
-  const int nblk = (T + kRPBlock - 1) / kRPBlock;
+  const int nblk = (int)(((int64_t)T + kRPBlock - 1) / kRPBlock);
   a.cnt = reinterpret_cast<int*>(static_cast<uint8_t*>(workspace) + kRPHeaderBytes);
   a.base = a.cnt + (size_t)nblk * E;
   a.nA = T == 0 ? 1 : nblk;  // T == 0: one workgroup writes the zero offsets
-  a.nC = (T + kRPRankTokens - 1) / kRPRankTokens;
+  a.nC = (int)(((int64_t)T + kRPRankTokens - 1) / kRPRankTokens);
   a.Ep = 1;
   while (a.Ep < E) a.Ep <<= 1;
   hipStream_t st = as_stream(stream);

@@ -124,7 +124,7 @@ extern "C" moe_status moe_router_logits(const uint16_t* x_bf16, const float* w_r
   clear_detail();
   MOE_REQUIRE(T >= 0 && E >= 1 && H > 0 && H % 64 == 0, MOE_ERR_SHAPE,
               "T=%d H=%d E=%d (H a positive multiple of 64, E >= 1)", T, H, E);
-  MOE_REQUIRE((T + 63) / 64 <= 0x7fffffff && (E + 63) / 64 <= 65535, MOE_ERR_UNSUPPORTED, "E=%d too large", E);
+  MOE_REQUIRE(((int64_t)E + 63) / 64 <= 65535, MOE_ERR_UNSUPPORTED, "E=%d too large", E);
   if (T == 0) return MOE_OK;
   MOE_REQUIRE(x_bf16 && w_router && logits, MOE_ERR_NULL, "x, w_router and logits are required");
   MOE_REQUIRE(aligned(x_bf16, 16) && aligned(w_router, 16) && aligned(logits, 4), MOE_ERR_ALIGN,
@@ -132,11 +132,11 @@ extern "C" moe_status moe_router_logits(const uint16_t* x_bf16, const float* w_r
   hipStream_t s = as_stream(stream);
   // 32-token tiles when 64-token ones would leave compute units without a
   // second workgroup
-  const unsigned ge = (unsigned)((E + 63) / 64);
-  if ((int64_t)((T + 63) / 64) * ge < 512)
+  const unsigned ge = (unsigned)(((int64_t)E + 63) / 64);
+  if (((int64_t)T + 63) / 64 * ge < 512)
     router_kernel<32><<<dim3((unsigned)((T + 31) / 32), ge), 256, 0, s>>>(x_bf16, w_router, T, H, E, logits);
   else
-    router_kernel<64><<<dim3((unsigned)((T + 63) / 64), ge), 256, 0, s>>>(x_bf16, w_router, T, H, E, logits);
+    router_kernel<64><<<dim3((unsigned)(((int64_t)T + 63) / 64), ge), 256, 0, s>>>(x_bf16, w_router, T, H, E, logits);
   return after_launch("moe_router_logits", s);
 }
 

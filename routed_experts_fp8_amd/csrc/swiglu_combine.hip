@@ -118,6 +118,8 @@ extern "C" moe_status swiglu(const float* gate_up, int64_t M, int32_t I, uint8_t
   clear_detail();
   MOE_REQUIRE(M >= 0 && I > 0 && I % 128 == 0, MOE_ERR_SHAPE, "M=%lld I=%d (I a positive multiple of 128)",
               (long long)M, I);
+  MOE_REQUIRE(elems_ok(M, 2 * (int64_t)I), MOE_ERR_UNSUPPORTED, "M=%lld x 2I=%lld above 2^40 elements",
+              (long long)M, 2 * (long long)I);
   if (M == 0) return MOE_OK;
   MOE_REQUIRE(gate_up && hq && hs, MOE_ERR_NULL, "gate_up, hq and hs are required");
   MOE_REQUIRE(aligned(gate_up, 16) && aligned(hq, 16) && aligned(hs, 4), MOE_ERR_ALIGN,
@@ -133,7 +135,9 @@ extern "C" moe_status moe_combine(const float* y_perm, const int32_t* dst_row,
                                   const float* topk_gate, const float* shared, int32_t T,
                                   int32_t K, int32_t H, uint16_t* out_bf16, void* stream) {
   clear_detail();
-  MOE_REQUIRE(T >= 0 && K >= 1 && H > 0 && H % 8 == 0, MOE_ERR_SHAPE, "T=%d K=%d H=%d (H % 8 == 0)", T, K, H);
+  MOE_REQUIRE(T >= 0 && K >= 1 && H > 0 && H % 8 == 0, MOE_ERR_SHAPE, "T=%d K=%d H=%d (H must be a positive multiple of 8)", T, K, H);
+  MOE_REQUIRE(elems_ok((int64_t)T * K, H), MOE_ERR_UNSUPPORTED, "T*K=%lld x H=%d above 2^40 elements",
+              (long long)T * K, H);
   if (T == 0) return MOE_OK;
   MOE_REQUIRE(y_perm && dst_row && topk_gate && out_bf16, MOE_ERR_NULL,
               "y_perm, dst_row, topk_gate and out_bf16 are required");

@@ -65,6 +65,8 @@ extern "C" moe_status fp8_block_transpose(const uint8_t* q, const float* scale, 
   clear_detail();
   MOE_REQUIRE(G >= 0 && rows > 0 && cols > 0 && rows % 128 == 0 && cols % 128 == 0, MOE_ERR_SHAPE,
               "G=%d rows=%d cols=%d (rows, cols positive multiples of 128)", G, rows, cols);
+  MOE_REQUIRE(elems_ok((int64_t)G * rows, cols), MOE_ERR_UNSUPPORTED, "G=%d x %d x %d above 2^40 elements", G,
+              rows, cols);
   if (G == 0) return MOE_OK;
   MOE_REQUIRE(q && scale && qt && scale_t, MOE_ERR_NULL, "q, scale, qt and scale_t are required");
   MOE_REQUIRE(aligned(q, 16) && aligned(qt, 16) && aligned(scale, 4) && aligned(scale_t, 4),

@@ -361,6 +361,7 @@ extern "C" moe_status moe_wgrad_padded_rows(int64_t M, int32_t G, int64_t* rows)
   clear_detail();
   MOE_REQUIRE(rows, MOE_ERR_NULL, "rows is required");
   MOE_REQUIRE(M >= 0 && G >= 1, MOE_ERR_SHAPE, "M=%lld G=%d", (long long)M, G);
+  MOE_REQUIRE(M <= kMaxElems, MOE_ERR_UNSUPPORTED, "M=%lld above 2^40", (long long)M);
   *rows = 128 * ((M + 127) / 128 + (int64_t)G);
   return MOE_OK;
 }

@@ -213,7 +213,11 @@ def _rand_idx(T, E, K, rng, skew=0.0):
 
 
 @pytest.mark.parametrize("T,E,K,H", [(1, 4, 2, 128), (255, 64, 8, 256), (256, 8, 2, 512), (257, 256, 8, 384),
-                                     (1000, 1024, 4, 128), (700, 16, 16, 128)])
+                                     (1000, 1024, 4, 128), (700, 16, 16, 128),
+                                     # many 256-token blocks: the scan splits each expert's blocks
+                                     # into runs (E = 128: 8 runs; E = 7: 128 runs, most empty;
+                                     # E = 1024: one run)
+                                     (20000, 128, 8, 128), (5000, 7, 3, 128), (3000, 1024, 4, 128)])
 def test_permute_bitexact(T, E, K, H):
     idx = _rand_idx(T, E, K, RNG, skew=0.05)
     xq = RNG.integers(0, 256, (T, H)).astype(np.uint8)
