@@ -593,19 +593,6 @@ __global__ __launch_bounds__(C::kThreads, C::kMinBlocks) void grouped_gemm_kerne
   __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 }
 
-// Compute units of the current device (looked up once per device; the
-// stored value is the same whichever thread stores it).
-int device_cu_count() {
-  static std::atomic<int> cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int n = cache[dev].load(std::memory_order_relaxed);
-  if (n == 0) {
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cache[dev].store(n, std::memory_order_relaxed);
-  }
-  return n;
-}
 
 template <int MODE, class C>
 moe_status launch_cfg(const uint8_t* aq, const float* as, const int* a_row, int64_t a_rows, const uint8_t* bq,

@@ -18,6 +18,8 @@ void clear_detail();
 // After enqueueing: hipGetLastError -> MOE_ERR_HIP; with MOEFP8_SYNC_CHECK=1
 // also synchronises `stream` and reports asynchronous errors.
 moe_status after_launch(const char* what, hipStream_t stream);
+// Compute units of the current device (256 if the runtime cannot say).
+int device_cu_count();
 
 inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 

@@ -1,6 +1,7 @@
 // Status strings, thread-local error detail and the post-launch check of the
 // libmoefp8 C ABI.
 #include <stdlib.h>
+#include <atomic>
 #include <string.h>
 
 #include "host_common.h"
@@ -35,6 +36,20 @@ moe_status after_launch(const char* what, hipStream_t stream) {
     if (e != hipSuccess) return fail(MOE_ERR_HIP, "%s: device error: %s", what, hipGetErrorString(e));
   }
   return MOE_OK;
+}
+
+// Compute units of the current device (looked up once per device; the
+// stored value is the same whichever thread stores it).
+int device_cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
 }
 
 }  // namespace moefp8

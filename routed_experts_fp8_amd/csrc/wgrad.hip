@@ -22,32 +22,35 @@
 //   index (gather), optionally times a per-row factor (the combine gate, for
 //   the down projection's output gradient), or as h = silu(g) * u of a
 //   float32 gate|up row (the forward's binary32 SwiGLU).
-// wgrad_kernel           one workgroup per 256x256 output tile of one expert,
-//   8 waves of 128 (input features) x 64 (output features), 2 waves per
-//   SIMD.  The tile's K is the expert's padded row count (one or two
-//   128-row chunks at the DeepSeek-V3 shape), so the kernel streams its
-//   output, and what bounds it is the traffic through each compute unit's
-//   vector-memory path (operand loads plus the float32 output).  Each
-//   chunk's operand rows and scales go straight from global memory into a
-//   2-stage LDS ring (global_load_lds, no register staging; 128-byte rows
-//   with the 16-byte XOR swizzle of the forward GEMM), so a workgroup reads
-//   each operand byte once: (256 + 256) x 128 bytes per chunk for 256 x 256
-//   outputs, against twice that per 128 x 128 outputs when every wave loads
-//   its own fragments.  Every chunk is multiplied with one
+// wgrad_kernel           256x256 output tiles of one expert, 8 waves of 128
+//   (input features) x 64 (output features), 2 waves per SIMD, one
+//   workgroup per compute unit walking its share of the tiles.  The tile's
+//   K is the expert's padded row count (one or two 128-row chunks at the
+//   DeepSeek-V3 shape), so the kernel streams its output, and what bounds
+//   it is the traffic through each compute unit's vector-memory path
+//   (operand loads plus the output).  Each chunk's operand rows and scales
+//   go straight from global memory into a 2-stage LDS ring (global_load_lds,
+//   no register staging; 128-byte rows with the 16-byte XOR swizzle of the
+//   forward GEMM), so a workgroup reads each operand byte once: (256 + 256)
+//   x 128 bytes per chunk for 256 x 256 outputs, against twice that per
+//   128 x 128 outputs when every wave loads its own fragments.  The ring
+//   runs across tile boundaries: the next tile's first chunk is loaded while
+//   the current tile is multiplied and stored, and no workgroup launch
+//   separates two tiles.  Every chunk is multiplied with one
 //   V_MFMA_SCALE_F32_16X16X128_F8F6F4 per 16x16 block with a zero
 //   accumulator and promoted with one FMA per output by the product of the
 //   two 128x1 scales (which vary along both output axes; stored tile-major,
 //   [padded row / 128, column], so a chunk's scales are contiguous).  The
 //   input operand sits on the instruction's row axis, so each lane holds 4
 //   consecutive input features of one output row and stores them as one
-//   16-byte (float32) or 8-byte (bf16) vector.  Tiles of one expert are
+//   16-byte float32 vector; for bf16 output two lanes trade halves first
+//   (a lane-row swap), so each lane still stores 16 bytes and each store
+//   writes 64 contiguous bytes of a row.  Tiles of one expert are
 //   consecutive and the logical tile order is dealt XCD by XCD; inside an
 //   expert the order is blocked (2 output-feature tiles by every
 //   input-feature tile), so the tiles in flight on one XCD share a few
 //   operand slabs, which stay in its L2 despite the output stream passing
-//   through it, and write long contiguous runs of the same output rows.  One tile per workgroup: a persistent walk would have to
-//   wait for the next tile's loads behind the previous tile's stores (one
-//   vector-memory counter counts both).
+//   through it, and write long contiguous runs of the same output rows.
 #include "host_common.h"
 #include "lds_dma.h"
 
@@ -210,6 +213,28 @@ __device__ __forceinline__ void store4(float* p, const float v[4], bool acc) {
   }
   *reinterpret_cast<float4*>(p) = o;
 }
+// 8 consecutive bf16 outputs (one 16-byte store), optionally added to the
+// values already there (each sum rounded once to bf16).
+__device__ __forceinline__ void store8(uint16_t* p, const float v[8], bool acc) {
+  float a[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = v[i];
+  if (acc) {
+    const uint4 old = *reinterpret_cast<const uint4*>(p);
+    const uint32_t w[4] = {old.x, old.y, old.z, old.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      a[2 * i] = a[2 * i] + __uint_as_float(w[i] << 16);
+      a[2 * i + 1] = a[2 * i + 1] + __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+  uint4 o;
+  o.x = bf16_rne_bits(a[0]) | (bf16_rne_bits(a[1]) << 16);
+  o.y = bf16_rne_bits(a[2]) | (bf16_rne_bits(a[3]) << 16);
+  o.z = bf16_rne_bits(a[4]) | (bf16_rne_bits(a[5]) << 16);
+  o.w = bf16_rne_bits(a[6]) | (bf16_rne_bits(a[7]) << 16);
+  *reinterpret_cast<uint4*>(p) = o;
+}
 __device__ __forceinline__ void store4(uint16_t* p, const float v[4], bool acc) {
   float a[4] = {v[0], v[1], v[2], v[3]};
   if (acc) {
@@ -223,70 +248,105 @@ __device__ __forceinline__ void store4(uint16_t* p, const float v[4], bool acc) 
   *reinterpret_cast<uint2*>(p) = o;
 }
 
-template <typename OT, bool kAcc>
+template <typename OT, bool kAcc, bool kPair>
 __global__ __launch_bounds__(kWgThreads, 2) void wgrad_kernel(const uint8_t* __restrict__ aq,
                                                              const float* __restrict__ as,
                                                              const uint8_t* __restrict__ bq,
                                                              const float* __restrict__ bs,
                                                              const int* __restrict__ poff, int Na, int Nb,
                                                              int64_t ld, int64_t n_tiles, int64_t per_xcd,
-                                                             OT* __restrict__ out) {
+                                                             int nwg, OT* __restrict__ out) {
   __shared__ __attribute__((aligned(1024))) uint8_t ring[2 * kWgStageBytes];
+  // XCD x (workgroup b runs on XCD b % 8) owns the logical tiles
+  // [x per_xcd, (x + 1) per_xcd); its nwg workgroups take every nwg-th one,
+  // so the tiles in flight on an XCD stay a window of about nwg neighbours
   const int64_t b = blockIdx.x;
-  const int64_t tile = (b & 7) * per_xcd + (b >> 3);  // workgroup b runs on XCD b % 8
-  if (tile >= n_tiles) return;
+  const int64_t xcd = b & 7;
+  const int64_t t_first = xcd * per_xcd + (b >> 3);
+  const int64_t t_end = (xcd + 1) * per_xcd < n_tiles ? (xcd + 1) * per_xcd : n_tiles;
   const int to_n = (Na + kWgTile - 1) / kWgTile, ti_n = (Nb + kWgTile - 1) / kWgTile;
   const int64_t per_g = (int64_t)to_n * ti_n;
-  const int g = (int)(tile / per_g);
-  const int rem = (int)(tile % per_g);
-  // blocked order inside the expert: blocks of kOB output-feature tiles, and
-  // inside a block the input-feature tile outermost, so the tiles an XCD runs
-  // at once share a few operand slabs of each kind instead of one A slab and
-  // every B slab (which the output stream would evict before their reuse)
-  const int ob = rem / (kOB * ti_n), r2 = rem % (kOB * ti_n);
-  const int obs = to_n - ob * kOB < kOB ? to_n - ob * kOB : kOB;  // tiles in this block
-  const int o0 = (ob * kOB + r2 % obs) * kWgTile, i0 = (r2 / obs) * kWgTile;
+  const int64_t nkb = ld / 128;
+  // tile -> expert, origin and chunk range.  Blocked order inside the
+  // expert: blocks of kOB output-feature tiles, and inside a block the
+  // input-feature tile outermost, so the tiles an XCD runs at once share a
+  // few operand slabs of each kind instead of one A slab and every B slab
+  // (which the output stream would evict before their reuse)
+  auto decode = [&](int64_t tile, int& g, int& o0, int& i0, int64_t& kb0, int& nk) {
+    g = (int)(tile / per_g);
+    const int rem = (int)(tile % per_g);
+    const int ob = rem / (kOB * ti_n), r2 = rem % (kOB * ti_n);
+    const int obs = to_n - ob * kOB < kOB ? to_n - ob * kOB : kOB;  // tiles in this block
+    o0 = (ob * kOB + r2 % obs) * kWgTile;
+    i0 = (r2 / obs) * kWgTile;
+    int64_t k0 = poff[g] / 128, k1 = poff[g + 1] / 128;
+    k0 = k0 < 0 ? 0 : (k0 > nkb ? nkb : k0);
+    k1 = k1 < k0 ? k0 : (k1 > nkb ? nkb : k1);
+    kb0 = k0;
+    nk = (int)(k1 - k0);
+  };
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform wave index
   const int q = lane >> 4, l16 = lane & 15;
-  const int64_t nkb = ld / 128;
-  int64_t kb0 = poff[g] / 128, kb1 = poff[g + 1] / 128;
-  kb0 = kb0 < 0 ? 0 : (kb0 > nkb ? nkb : kb0);
-  kb1 = kb1 < kb0 ? kb0 : (kb1 > nkb ? nkb : kb1);
-  const int nk = (int)(kb1 - kb0);
 
   // ---- issue side: wave w fetches In rows and Out rows 32w .. 32w + 31 of
   // the tile (4 slices of 8 rows each) and one scale slice; rows past Nb / Na
   // re-read the last row.  Lane: row 8j + lane / 8 of slice j, physical
-  // 16-byte piece lane % 8, holding the swizzled logical piece.
+  // 16-byte piece lane % 8, holding the swizzled logical piece.  Scales:
+  // waves 0-3 fetch In scales 64w .., waves 4-7 Out scales 64(w - 4) ..
   const int rsub = lane >> 3, c16 = (lane & 7) ^ rsub;
-  int64_t in_row[4], out_row[4];  // scalar: first (clamped) row of each slice
-  uint32_t in_off[4], out_off[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = 32 * w + 8 * j;
-    const int ri = min(i0 + r, Nb - 1), ro = min(o0 + r, Na - 1);
-    in_row[j] = (int64_t)ri * ld;
-    out_row[j] = (int64_t)ro * ld;
-    in_off[j] = (uint32_t)((int64_t)(min(i0 + r + rsub, Nb - 1) - ri) * ld + c16 * 16);
-    out_off[j] = (uint32_t)((int64_t)(min(o0 + r + rsub, Na - 1) - ro) * ld + c16 * 16);
-  }
-  // scales: waves 0-3 fetch In scales 64w .., waves 4-7 Out scales 64(w - 4) ..
   const bool s_in = w < 4;
   const int s_n = s_in ? Nb : Na;
-  const int s_first = min((s_in ? i0 : o0) + 64 * (w & 3), s_n - 1);
-  const uint32_t s_off = (uint32_t)(min((s_in ? i0 : o0) + 64 * (w & 3) + lane, s_n - 1) - s_first) * 4u;
-  const float* s_src = (s_in ? bs : as) + s_first;
   const uint32_t s_lds = (s_in ? kWgOffSIn : kWgOffSOut) + 256 * (w & 3);
   const uint32_t ring_lds = __builtin_amdgcn_readfirstlane(lds_addr(ring));
-  auto issue = [&](int64_t kb, int stage) {
+  auto issue = [&](int o0, int i0, int64_t kb, int stage) {
     const uint32_t st = ring_lds + stage * kWgStageBytes;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(bq + in_row[j] + kb * 128, in_off[j], st + kWgOffIn + (4 * w + j) * 1024);
+    for (int j = 0; j < 4; ++j) {
+      const int r = 32 * w + 8 * j;
+      const int ri = min(i0 + r, Nb - 1);  // scalar: the slice's first (clamped) row
+      const uint32_t off = (uint32_t)((int64_t)(min(i0 + r + rsub, Nb - 1) - ri) * ld + c16 * 16);
+      dma16(bq + (int64_t)ri * ld + kb * 128, off, st + kWgOffIn + (4 * w + j) * 1024);
+    }
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dma16(aq + out_row[j] + kb * 128, out_off[j], st + kWgOffOut + (4 * w + j) * 1024);
-    dma4(s_src + kb * s_n, s_off, st + s_lds);
+    for (int j = 0; j < 4; ++j) {
+      const int r = 32 * w + 8 * j;
+      const int ro = min(o0 + r, Na - 1);
+      const uint32_t off = (uint32_t)((int64_t)(min(o0 + r + rsub, Na - 1) - ro) * ld + c16 * 16);
+      dma16(aq + (int64_t)ro * ld + kb * 128, off, st + kWgOffOut + (4 * w + j) * 1024);
+    }
+    const int sr = (s_in ? i0 : o0) + 64 * (w & 3);
+    const int s_first = min(sr, s_n - 1);
+    const uint32_t s_off = (uint32_t)(min(sr + lane, s_n - 1) - s_first) * 4u;
+    dma4((s_in ? bs : as) + s_first + kb * s_n, s_off, st + s_lds);
   };
+  // The workgroup's chunk stream is its tiles' chunks in order; the issue
+  // cursor (tile it, chunk ikb) runs one chunk ahead of the multiplies, so a
+  // tile's first chunk is in flight while the previous tile is multiplied
+  // and stored.  Tiles of experts without rows have no chunks.
+  int64_t it = t_first, ikb = 0, ikb_end = 0;
+  int io0 = 0, ii0 = 0;
+  auto seek = [&]() {
+    for (; it < t_end; it += nwg) {
+      int g, nk;
+      int64_t kb0;
+      decode(it, g, io0, ii0, kb0, nk);
+      if (nk > 0) {
+        ikb = kb0, ikb_end = kb0 + nk;
+        return;
+      }
+    }
+  };
+  auto issue_next = [&](int stage) {
+    if (it >= t_end) return;
+    issue(io0, ii0, ikb, stage);
+    if (++ikb == ikb_end) {
+      it += nwg;
+      seek();
+    }
+  };
+  seek();
+  issue_next(0);
 
   // ---- multiply side: wave w owns In rows wi .. wi + 127 (instruction rows,
   // 8 fragments) by Out rows wo .. wo + 63 (instruction columns, 4 fragments)
@@ -297,58 +357,85 @@ __global__ __launch_bounds__(kWgThreads, 2) void wgrad_kernel(const uint8_t* __r
   for (int fi = 0; fi < 8; ++fi)
 #pragma unroll
     for (int fo = 0; fo < 4; ++fo) acc[fi][fo] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  // two stages: chunks 0 and 1 are issued up front, chunk c + 1 (c >= 1) once
-  // every wave is done with chunk c - 1, whose stage it takes
-  if (nk > 0) issue(kb0, 0);
-  if (nk > 1) issue(kb0 + 1, 1);
-  for (int c = 0; c < nk; ++c) {
-    // this wave's loads of chunk c have landed (chunk 1 may still fly at c = 0;
-    // loads complete in issue order) and its reads of chunk c - 1 are done;
-    // after the barrier the same holds for every wave.  The asm's memory
-    // clobber keeps the LDS reads below on this side of it.
-    static_assert(kWgDmaPerChunk == 9, "the wait below counts one chunk's loads");
-    if (c == 0 && nk > 1)
-      asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    else
+  int qs = 0;  // position in the chunk stream; its ring stage is qs & 1
+  for (int64_t tile = t_first; tile < t_end; tile += nwg) {
+    int g, o0, i0, nk;
+    int64_t kb0;
+    decode(tile, g, o0, i0, kb0, nk);
+    for (int c = 0; c < nk; ++c, ++qs) {
+      // this wave's loads of chunk qs (its only DMA in flight) have landed
+      // and its reads of chunk qs - 1 are done; after the barrier the same
+      // holds for every wave, so chunk qs + 1 may take chunk qs - 1's stage.
+      // The asm's memory clobber keeps the LDS reads below on this side.
       asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (c >= 1 && c + 1 < nk) issue(kb0 + c + 1, (c + 1) & 1);
-    const uint8_t* st = ring + (c & 1) * kWgStageBytes;
-    const float* sSI = reinterpret_cast<const float*>(st + kWgOffSIn);
-    const float* sSO = reinterpret_cast<const float*>(st + kWgOffSOut);
-    v8i bo[4];
-    float so[4];
-#pragma unroll
-    for (int fo = 0; fo < 4; ++fo) {
-      bo[fo] = lds_operand(st + kWgOffOut + (wo + 16 * fo) * 128, lane_lo, lane_hi);
-      so[fo] = sSO[wo + 16 * fo + l16];
-    }
-#pragma unroll
-    for (int fi = 0; fi < 8; ++fi) {
-      const v8i ai = lds_operand(st + kWgOffIn + (wi + 16 * fi) * 128, lane_lo, lane_hi);
-      // In rows wi + 16 fi + 4q + v: four consecutive scales
-      const float4 s4 = *reinterpret_cast<const float4*>(sSI + wi + 16 * fi + 4 * q);
-      const float si[4] = {s4.x, s4.y, s4.z, s4.w};
+      issue_next((qs + 1) & 1);
+      const uint8_t* st = ring + (qs & 1) * kWgStageBytes;
+      const float* sSI = reinterpret_cast<const float*>(st + kWgOffSIn);
+      const float* sSO = reinterpret_cast<const float*>(st + kWgOffSOut);
+      v8i bo[4];
+      float so[4];
 #pragma unroll
       for (int fo = 0; fo < 4; ++fo) {
-        const v4f p = mfma_chunk(ai, bo[fo]);
+        bo[fo] = lds_operand(st + kWgOffOut + (wo + 16 * fo) * 128, lane_lo, lane_hi);
+        so[fo] = sSO[wo + 16 * fo + l16];
+      }
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[fi][fo][v] = __builtin_fmaf(p[v], si[v] * so[fo], acc[fi][fo][v]);
+      for (int fi = 0; fi < 8; ++fi) {
+        const v8i ai = lds_operand(st + kWgOffIn + (wi + 16 * fi) * 128, lane_lo, lane_hi);
+        // In rows wi + 16 fi + 4q + v: four consecutive scales
+        const float4 s4 = *reinterpret_cast<const float4*>(sSI + wi + 16 * fi + 4 * q);
+        const float si[4] = {s4.x, s4.y, s4.z, s4.w};
+#pragma unroll
+        for (int fo = 0; fo < 4; ++fo) {
+          const v4f p = mfma_chunk(ai, bo[fo]);
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[fi][fo][v] = __builtin_fmaf(p[v], si[v] * so[fo], acc[fi][fo][v]);
+        }
       }
     }
-  }
-  // every load of this workgroup has landed (the last wait was vmcnt(0), or
-  // nothing was issued), so its LDS can be released after the stores
-  OT* og = out + (int64_t)g * Na * Nb;
+    // A wave's 128 x 64 share is all inside the output or all past Na / Nb
+    // (both multiples of 128, tile origins multiples of 256).  Lane (q, l16)
+    // holds Out row wo + 16 fo + l16, In columns wi + 16 fi + 4q .. + 3.
+    if (o0 + wo < Na && i0 + wi < Nb) {
+      OT* og = out + (int64_t)g * Na * Nb;
+      if constexpr (kPair) {
+        // bf16 into a 16-byte aligned output: lanes of the row pair
+        // (q, q ^ 1) trade halves of the instruction-tile pair (fi, fi + 1)
+        // with one lane-row swap per value, so even q holds columns
+        // 16 fi + 4q .. + 7 and odd q columns 16 fi + 4q + 12 .. + 19, and each
+        // 16-byte store writes 64 contiguous bytes of an output row (the
+        // 8-byte stores wrote 32, at the same count of write requests)
 #pragma unroll
-  for (int fo = 0; fo < 4; ++fo) {
-    if (o0 + wo + 16 * fo >= Na) break;  // rows past Na: a half tile
+        for (int fo = 0; fo < 4; ++fo) {
 #pragma unroll
-    for (int fi = 0; fi < 8; ++fi) {
-      if (i0 + wi + 16 * fi >= Nb) break;
-      const float v[4] = {acc[fi][fo][0], acc[fi][fo][1], acc[fi][fo][2], acc[fi][fo][3]};
-      store4(og + (int64_t)(o0 + wo + 16 * fo + l16) * Nb + i0 + wi + 16 * fi + 4 * q, v, kAcc);
+          for (int fi = 0; fi < 8; fi += 2) {
+            float v[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(acc[fi][fo][e]),
+                                                              __float_as_uint(acc[fi + 1][fo][e]), false, false);
+              v[e] = __uint_as_float(r[0]);
+              v[4 + e] = __uint_as_float(r[1]);
+            }
+            store8(og + (int64_t)(o0 + wo + 16 * fo + l16) * Nb + i0 + wi + 16 * fi + 4 * q + 12 * (q & 1), v,
+                   kAcc);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int fo = 0; fo < 4; ++fo) {
+#pragma unroll
+          for (int fi = 0; fi < 8; ++fi) {
+            const float v[4] = {acc[fi][fo][0], acc[fi][fo][1], acc[fi][fo][2], acc[fi][fo][3]};
+            store4(og + (int64_t)(o0 + wo + 16 * fo + l16) * Nb + i0 + wi + 16 * fi + 4 * q, v, kAcc);
+          }
+        }
+      }
     }
+#pragma unroll
+    for (int fi = 0; fi < 8; ++fi)
+#pragma unroll
+      for (int fo = 0; fo < 4; ++fo) acc[fi][fo] = v4f{0.f, 0.f, 0.f, 0.f};
   }
 }
 
@@ -433,15 +520,21 @@ extern "C" moe_status grouped_wgrad_fp8(const uint8_t* aq, const float* as, cons
                   aligned(padded_offsets, 4) && aligned(c, c_dtype == MOE_F32 ? 16 : 8),
               MOE_ERR_ALIGN, "aq, bq (and a float32 c) need 16-byte alignment, a bf16 c 8-byte");
   hipStream_t s = as_stream(stream);
+  // one workgroup per compute unit (its LDS ring fills one), each walking
+  // its share of its XCD's tiles
   const int64_t per_xcd = (n_tiles + 7) / 8;
-  const unsigned grid = (unsigned)(8 * per_xcd);
-#define MOE_WGRAD_LAUNCH(OT, ACC)                                                                          \
-  wgrad_kernel<OT, ACC><<<grid, kWgThreads, 0, s>>>(aq, as, bq, bs, padded_offsets, Na, Nb, ld, n_tiles, per_xcd, \
-                                            static_cast<OT*>(c))
+  int64_t nwg = (device_cu_count() + 7) / 8;
+  if (nwg > per_xcd) nwg = per_xcd;
+  const unsigned grid = (unsigned)(8 * nwg);
+#define MOE_WGRAD_LAUNCH(OT, ACC, PAIR)                                                                     \
+  wgrad_kernel<OT, ACC, PAIR><<<grid, kWgThreads, 0, s>>>(aq, as, bq, bs, padded_offsets, Na, Nb, ld, n_tiles, \
+                                                          per_xcd, (int)nwg, static_cast<OT*>(c))
   if (c_dtype == MOE_F32) {
-    if (accumulate) MOE_WGRAD_LAUNCH(float, true); else MOE_WGRAD_LAUNCH(float, false);
+    if (accumulate) MOE_WGRAD_LAUNCH(float, true, false); else MOE_WGRAD_LAUNCH(float, false, false);
+  } else if (aligned(c, 16)) {
+    if (accumulate) MOE_WGRAD_LAUNCH(uint16_t, true, true); else MOE_WGRAD_LAUNCH(uint16_t, false, true);
   } else {
-    if (accumulate) MOE_WGRAD_LAUNCH(uint16_t, true); else MOE_WGRAD_LAUNCH(uint16_t, false);
+    if (accumulate) MOE_WGRAD_LAUNCH(uint16_t, true, false); else MOE_WGRAD_LAUNCH(uint16_t, false, false);
   }
 #undef MOE_WGRAD_LAUNCH
   return after_launch("grouped_wgrad_fp8", s);

@@ -165,6 +165,44 @@ def test_wgrad_gemm_many_groups():
     _check_wgrad(np_(c), C, Mag, _wgrad_bound(aq, as_, bq, bs, p), "wgrad 64 experts")
 
 
+
+def test_wgrad_tile_walk_and_output_paths():
+    """100 experts of 0-300 rows at Na = 384, Nb = 640 (half tiles on both
+    axes): 600 output tiles, so each workgroup walks two or three tiles,
+    empty experts' tiles among them, with the next tile's loads in flight
+    while the current one is stored.  float32 against the oracle; bf16 as
+    the float32 result rounded once, through both store paths (16-byte
+    aligned output: lanes trade halves for 16-byte stores; 8-byte aligned
+    output: 8-byte stores) and with accumulation onto bf16 values
+    (float32 add, then one rounding)."""
+    rng = np.random.default_rng(77)
+    sizes = list(rng.integers(0, 301, 100))
+    sizes[0] = sizes[17] = sizes[99] = 0
+    sizes[50] = 300
+    Na, Nb = 384, 640
+    aq, as_, bq, bs, p = _wgrad_problem(sizes, Na, Nb, rng)
+    C, Mag = O.wgrad_gemm(aq, as_, bq, bs, p)
+    ld = R.moe_wgrad_padded_rows(sum(sizes), len(sizes))
+    args = [to_dev(_pad_ld(aq, ld)), _scales_dev(as_, ld), to_dev(_pad_ld(bq, ld)), _scales_dev(bs, ld), to_dev(p)]
+    c32 = R.grouped_wgrad_fp8(*args)
+    _check_wgrad(np_(c32), C, Mag, _wgrad_bound(aq, as_, bq, bs, p), "wgrad tile walk")
+    G = len(sizes)
+    want = c32.to(torch.bfloat16)
+    n = G * Na * Nb
+    old_vals = torch.from_numpy(rng.standard_normal(n).astype(F32)).to(dev()).to(torch.bfloat16)
+    want_acc = (c32.reshape(-1) + old_vals.float()).to(torch.bfloat16).reshape(G, Na, Nb)
+    for shift, aligned16 in ((0, True), (4, False)):     # 4 bf16 = 8 bytes past a 256-byte boundary
+        buf = torch.full((n + 8,), float("nan"), dtype=torch.bfloat16, device=dev())
+        c = buf[shift:shift + n].view(G, Na, Nb)
+        assert (c.data_ptr() % 16 == 0) == aligned16
+        R.grouped_wgrad_fp8(*args, c=c)
+        assert torch.equal(c, want), f"bf16 output, 16-byte aligned {aligned16}"
+        c.copy_(old_vals.view(G, Na, Nb))
+        R.grouped_wgrad_fp8(*args, c=c, accumulate=True)
+        assert torch.equal(c, want_acc), f"bf16 accumulate, 16-byte aligned {aligned16}"
+        assert torch.isnan(buf[:shift].float()).all() and torch.isnan(buf[shift + n:].float()).all()
+
+
 def _deq(q, s):
     return O.e4m3_decode(q) * np.repeat(np.asarray(s, np.float64), 128, axis=1)
 
@@ -328,3 +366,5 @@ def test_quant_and_wgrad_at_the_group_limit():
     C, Mag = O.wgrad_gemm(aq, as_, bq, bs, p)
     _check_wgrad(c, C, Mag, _wgrad_bound(aq, as_, bq, bs, p), "wgrad 1024 experts")
     assert np.all(c[sizes == 0] == 0)
+    cb = R.grouped_wgrad_fp8(qt, st, qt2, st2, pg, out_dtype=torch.bfloat16)
+    assert torch.equal(cb, torch.from_numpy(c.astype(F32)).to(dev()).to(torch.bfloat16))
