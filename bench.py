@@ -137,6 +137,24 @@ def dense_fp8_gemm_rate(torch, n=8192, reps=20):
                 frac_mfma=2 * n ** 3 / ms / 1e9 / FP8_PEAK_TFLOPS)
 
 
+def mfma_probe_rate(torch, R, iters=20000, reps=5):
+    """The library's matrix-core probe: 8 independent chains of FP8 matrix
+    instructions per wave on register operands, no memory traffic, at the
+    grouped GEMM's occupancy (one 8-wave workgroup per compute unit, 2 waves
+    per SIMD) and at 8 waves per SIMD: the device's own FP8 ceiling beside
+    the 5.0 PFLOP/s datasheet figure."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = {}
+    for tag, per_cu in (("2_waves_per_simd", 1), ("8_waves_per_simd", 4)):
+        blocks = cus * per_cu
+        buf = torch.empty(blocks * 64 * 8, dtype=torch.float32, device="cuda")
+        fl = R.moe_probe_mfma_fp8(iters, blocks, 8, out=buf)[1]
+        ms = time_op(lambda: R.moe_probe_mfma_fp8(iters, blocks, 8, out=buf), reps, torch)
+        out[tag] = dict(blocks=blocks, waves_per_block=8, ms=ms, TFLOPs=fl / ms / 1e9,
+                        frac_mfma=fl / ms / 1e9 / FP8_PEAK_TFLOPS)
+    return out
+
+
 def wgrad_bytes(E, H, I, wg):
     """Algorithmic bytes of the down and gate|up weight-gradient launches:
     float32 gradients written once, the two 128x1 operands read once over
@@ -835,6 +853,8 @@ def main():
         extra["measured_copy"] = copy_rate(torch)
         log("measured FP8 matrix rate: a dense vendor-library FP8 GEMM")
         extra["measured_dense_fp8_gemm"] = dense_fp8_gemm_rate(torch)
+        log("measured FP8 matrix-core ceiling: the library's register-only probe")
+        extra["measured_mfma_fp8_probe"] = mfma_probe_rate(torch, R)
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle, bounded sample)")

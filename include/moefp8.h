@@ -607,6 +607,25 @@ MOE_API moe_status moe_router_logits(const uint16_t* x_bf16, const float* w_rout
 MOE_API moe_status moe_bias_update(const int32_t* expert_offsets, int32_t E, float gamma, float* bias,
                            void* stream);
 
+/*
+ * moe_probe_mfma_fp8 -- measurement helper, not a step of the layer: the
+ * FP8 matrix cores' own ceiling on this device (the figure the grouped
+ * GEMMs' rates are read against beside the datasheet peak).  `blocks`
+ * workgroups of `waves_per_block` waves each run 8 independent chains of
+ * `iters` V_MFMA_SCALE_F32_16X16X128_F8F6F4 on register operands whose every
+ * E4M3 code is `code`; each lane then writes the sum of its accumulators to
+ * out[64 * waves_per_block * block + lane] (so for a code of value v that sum
+ * is exactly 4096 v^2 iters while it stays an integer below 2^24), and
+ * *flops (host) receives the launch's flop count, 8 * 65536 per wave and
+ * iteration.  Time it with events on `stream`.
+ *
+ *  out f32 [blocks * 64 * waves_per_block] (device, written), flops (host).
+ *  0 <= iters <= 2^32, 1 <= blocks <= 2^20, 1 <= waves_per_block <= 16.
+ * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_ALIGN (out 4-byte).
+ */
+MOE_API moe_status moe_probe_mfma_fp8(uint8_t code, int64_t iters, int32_t blocks, int32_t waves_per_block,
+                                      float* out, double* flops, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -68,6 +68,8 @@ _SIGNATURES = {
                                  _i64, _c_void_p, _i32, _i32, _c_void_p]),
     "moe_router_logits": (_i32, [_c_void_p, _c_void_p, _i32, _i32, _i32, _c_void_p, _c_void_p]),
     "moe_bias_update": (_i32, [_c_void_p, _i32, ctypes.c_float, _c_void_p, _c_void_p]),
+    "moe_probe_mfma_fp8": (_i32, [ctypes.c_uint8, _i64, _i32, _i32, _c_void_p, ctypes.POINTER(ctypes.c_double),
+                                  _c_void_p]),
 }
 
 
@@ -577,3 +579,17 @@ def moe_bias_update(expert_offsets, gamma, bias):
     _need(bias, "bias", torch.float32, (E,))
     _check("moe_bias_update", lib.moe_bias_update(_p(expert_offsets), E, float(gamma), _p(bias), _stream()))
     return bias
+
+
+def moe_probe_mfma_fp8(iters, blocks, waves_per_block, code=0x38, out=None):
+    """Measurement helper (not a layer step): `blocks` workgroups of
+    `waves_per_block` waves run 8 chains of `iters` FP8 matrix instructions
+    on register operands (every code `code`); returns (out, flops) with out
+    the per-lane accumulator sums [blocks * 64 * waves_per_block] and flops
+    the launch's flop count."""
+    n = blocks * 64 * waves_per_block
+    out = _out(out, "out", (n,), torch.float32, torch.device("cuda", torch.cuda.current_device()))
+    fl = ctypes.c_double(0.0)
+    _check("moe_probe_mfma_fp8", lib.moe_probe_mfma_fp8(int(code), int(iters), int(blocks), int(waves_per_block),
+                                                         _p(out), ctypes.byref(fl), _stream()))
+    return out, fl.value

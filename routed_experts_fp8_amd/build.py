@@ -28,7 +28,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 SOURCES = ["status.cpp", "quant.hip", "transpose.hip", "route.hip", "permute.hip", "route_permute.hip",
-           "swiglu_combine.hip", "gemm.hip", "backward.hip", "wgrad.hip", "router.hip"]
+           "swiglu_combine.hip", "gemm.hip", "backward.hip", "wgrad.hip", "router.hip", "probe.hip"]
 
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

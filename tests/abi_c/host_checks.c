@@ -152,6 +152,18 @@ int main(void) {
   CHECK(moe_bias_update(P, 0, 0.1f, P, S), SHP);
   CHECK(moe_bias_update(P, 8, 0.1f, P2, S), ALI);
 
+  /* measurement helper */
+  {
+    double fl = 0.0;
+    CHECK(moe_probe_mfma_fp8(0x38, 10, 0, 8, P, &fl, S), SHP);
+    CHECK(moe_probe_mfma_fp8(0x38, -1, 1, 8, P, &fl, S), SHP);
+    CHECK(moe_probe_mfma_fp8(0x38, INT64_MAX, 1, 8, P, &fl, S), SHP);
+    CHECK(moe_probe_mfma_fp8(0x38, 10, 1, 17, P, &fl, S), SHP);
+    CHECK(moe_probe_mfma_fp8(0x38, 10, 1, 8, NULL, &fl, S), NUL);
+    CHECK(moe_probe_mfma_fp8(0x38, 10, 1, 8, P, NULL, S), NUL);
+    CHECK(moe_probe_mfma_fp8(0x38, 10, 1, 8, P2, &fl, S), ALI);
+  }
+
   printf("%d checks, %d failed\n%s\n", checks, failures, failures ? "FAILED" : "PASSED");
   return failures ? 1 : 0;
 }

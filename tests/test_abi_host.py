@@ -237,6 +237,18 @@ def test_router_errors():
     assert b(P, 8, 0.1, ctypes.c_void_p(0x10002), S) == ALIGN
 
 
+def test_probe_argument_errors():
+    pr = L.lib.moe_probe_mfma_fp8
+    fl = ctypes.c_double(0.0)
+    assert pr(0x38, 10, 0, 8, P, ctypes.byref(fl), S) == SHAPE          # no workgroup
+    assert pr(0x38, -1, 1, 8, P, ctypes.byref(fl), S) == SHAPE
+    assert pr(0x38, 2**40, 1, 8, P, ctypes.byref(fl), S) == SHAPE       # iterations above 2^32
+    assert pr(0x38, 10, 1, 17, P, ctypes.byref(fl), S) == SHAPE         # more than 16 waves
+    assert pr(0x38, 10, 1, 8, N0, ctypes.byref(fl), S) == NULL
+    assert pr(0x38, 10, 1, 8, P, None, S) == NULL
+    assert pr(0x38, 10, 1, 8, ctypes.c_void_p(0x10002), ctypes.byref(fl), S) == ALIGN
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     """Without the built library the binding raises instead of falling back."""
     monkeypatch.setattr(L, "LIB_PATH", str(tmp_path / "libmoefp8.so"))
