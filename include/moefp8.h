@@ -565,7 +565,9 @@ MOE_API moe_status quant_act_128x1_grouped_e4m3(const void* x, moe_dtype x_dtype
  *  most 2^29.
  * Errors: MOE_ERR_NULL, MOE_ERR_SHAPE, MOE_ERR_UNSUPPORTED (dtype, G, ld above
  *         2^29, more than 2^31 - 8 output tiles of 256 x 256), MOE_ERR_ALIGN
- *         (aq, bq 16-byte; c 16-byte for f32, 8-byte for bf16).
+ *         (aq, bq 16-byte; c 16-byte for f32, 8-byte for bf16; a bf16 c
+ *         that is 16-byte aligned is written with 16-byte stores, faster,
+ *         with the same values).
  */
 MOE_API moe_status grouped_wgrad_fp8(const uint8_t* aq, const float* as, const uint8_t* bq, const float* bs,
                              const int32_t* padded_offsets, int32_t G, int32_t Na, int32_t Nb, int64_t ld,
