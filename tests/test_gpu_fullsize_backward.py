@@ -146,3 +146,14 @@ def test_fullsize_dsv3_backward_and_weight_gradients():
                            *g_d1t, *g_xt, o13)
         stats.append((e, n, flip, r2, r13))
     print("expert, rows, dC1 code flips, dW2 / dW13 worst err/mag:", stats)
+    # bf16 weight gradients of every expert at full size (the 16-byte store
+    # path of the persistent tile walk): exactly the float32 results rounded
+    # once to nearest-even
+    wb = wg.buf
+    for name, ops, ref in (("dW2", (wb["dc2t"], wb["dc2ts"], wb["ht"], wb["hts"]), out["dw2"]),
+                           ("dW13", (wb["d1t"], wb["d1ts"], wb["xt"], wb["xts"]), out["dw13"])):
+        cb = R.grouped_wgrad_fp8(*ops, wb["poff"], out_dtype=torch.bfloat16)
+        assert cb.data_ptr() % 16 == 0
+        for g in range(E):
+            assert torch.equal(cb[g], ref[g].to(torch.bfloat16)), f"bf16 {name} expert {g}"
+        del cb
