@@ -122,6 +122,10 @@ __global__ __launch_bounds__(256) void quant128x1_kernel(
     const XT* __restrict__ x, int64_t ldx, int64_t x_rows, int C, const int* __restrict__ row_index,
     const float* __restrict__ row_scale, const int* __restrict__ offsets, const int* __restrict__ poff, int G,
     int64_t M, int64_t ld, uint8_t* __restrict__ qt, float* __restrict__ st) {
+  // [column][row]; a row index is stored XOR 4 ((column / 8) % 8), which
+  // keeps every aligned group of 4 rows contiguous (the float4 reads below)
+  // and spreads the transposing 4-byte writes of a wave over all 32 banks
+  // (2 lanes per bank instead of 8)
   __shared__ float tile[64][132];
   // column blocks fastest: consecutive workgroups read adjacent 128-byte
   // pieces of the same source rows (measured 5-10 % faster than row tiles
@@ -177,7 +181,7 @@ __global__ __launch_bounds__(256) void quant128x1_kernel(
         }
       }
 #pragma unroll
-      for (int i = 0; i < VW; ++i) tile[VW * cq + i][j] = v[i];
+      for (int i = 0; i < VW; ++i) tile[VW * cq + i][j ^ (4 * (((VW * cq + i) >> 3) & 7))] = v[i];
     }
   }
   __syncthreads();
@@ -185,7 +189,7 @@ __global__ __launch_bounds__(256) void quant128x1_kernel(
   float v[32];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const float4 f = *reinterpret_cast<const float4*>(&tile[c][32 * qq + 4 * i]);
+    const float4 f = *reinterpret_cast<const float4*>(&tile[c][(32 * qq + 4 * i) ^ (4 * ((c >> 3) & 7))]);
     v[4 * i] = f.x, v[4 * i + 1] = f.y, v[4 * i + 2] = f.z, v[4 * i + 3] = f.w;
   }
   float amax = 0.f;
